@@ -1,0 +1,100 @@
+"""Compile the native parts in-tree.
+
+* ``_lib/libattn.so``      the HIP kernels for gfx950 and the C ABI
+                           (``include/attn.h``), built with hipcc.
+* ``_lib/libattn_gen.so``  the seeded input generator (plain C, gcc).
+
+Both are always rebuilt when :func:`build_all` is called.  Loading code never
+builds: it raises if a library is missing.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+LIBDIR = PKG / "_lib"
+INCLUDE = ROOT / "include"
+
+HIP_SOURCES = [
+    CSRC / "attn_api.hip",
+    CSRC / "prefill_bf16.hip",
+    CSRC / "prefill_f32.hip",
+    CSRC / "decode_bf16.hip",
+]
+HIP_HEADERS = [CSRC / "kernel_common.h", INCLUDE / "attn.h"]
+
+# gfx950 only.  Packed fp32 VALU ops are switched off for all device code.
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics",
+]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def _run(cmd: list[str]) -> None:
+    print("[build]", " ".join(str(c) for c in cmd), flush=True)
+    subprocess.run([str(c) for c in cmd], check=True)
+
+
+def build_gen() -> Path:
+    LIBDIR.mkdir(exist_ok=True)
+    out = LIBDIR / "libattn_gen.so"
+    tmp = out.with_suffix(".so.tmp")
+    _run(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-pthread",
+          str(CSRC / "gen" / "normal_gen.c"), "-o", str(tmp), "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build_hip(jobs: int = 4) -> Path:
+    LIBDIR.mkdir(exist_ok=True)
+    objdir = LIBDIR / "obj"
+    objdir.mkdir(exist_ok=True)
+    hipcc = _hipcc()
+    objs = []
+    procs = []
+    for src in HIP_SOURCES:
+        obj = objdir / (src.stem + ".o")
+        objs.append(obj)
+        cmd = [hipcc, *HIP_FLAGS, "-I", str(INCLUDE), "-I", str(CSRC), "-c", str(src), "-o", str(obj)]
+        print("[build]", " ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+        if len(procs) >= jobs:
+            if procs.pop(0).wait() != 0:
+                raise subprocess.CalledProcessError(1, "hipcc")
+    for p in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(1, "hipcc")
+    out = LIBDIR / "libattn.so"
+    tmp = out.with_suffix(".so.tmp")
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)])
+    os.replace(tmp, out)
+    return out
+
+
+def build_all() -> None:
+    build_gen()
+    build_hip()
+
+
+if __name__ == "__main__":
+    build_all()
+    sys.exit(0)
