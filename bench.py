@@ -1,0 +1,253 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * prefill: Llama-3-8B-shaped causal GQA, B=1 H_q=32 H_kv=8 T=8192 D=128,
+    bf16 (attn_fwd_prefill, one kernel);
+  * decode:  B=64 H_q=32 H_kv=8, one query token against 4096 cached keys,
+    D=128, bf16 (attn_fwd_decode: split kernel + combine kernel).
+Inputs are seeded N(0,1) tensors, resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is the prefill throughput in TFLOP/s with
+causal FLOPs counted once (4*D per visible (query, key) pair per q head);
+the decode KV-read rate in GB/s is reported beside it.  Kernel durations come
+from HIP events recorded on the stream the kernels run on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "attention fwd TFLOP/s (causal GQA T=8K prefill); decode KV-read GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILES = ROOT / "profiles"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(Path(p).read_bytes())
+    return h.hexdigest()
+
+
+def traffic_from_profile(name, digest):
+    """Measured HBM bytes per launch from the committed counter summary, or
+    None when it is missing or was taken on different kernel source."""
+    f = PROFILES / f"{name}_traffic.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("source_sha256") != digest:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s=15.0):
+    """The CPU oracle, timed on this host on a bounded sample of the prefill
+    workload: q heads in order, every 4th query row, until the budget is
+    spent (at least one head)."""
+    import numpy as np
+    import oracle
+    from transformer_scaled_dot_flash_amd import inputs
+    from transformer_scaled_dot_flash_amd.workloads import PREFILL_HEADLINE as w
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    q, k, v = w.make_inputs()
+    Q, K, V = (inputs.as_f64(x, w.dtype) for x in (q, k, v))
+    rows = np.arange(0, w.T_q, 4)
+    flop_per_head = sum(4 * w.D * (int(i) + 1) for i in rows)
+    done = 0
+    t0 = time.perf_counter()
+    for h in range(w.H_q):
+        oracle.attention(Q, K, V, w.scale, w.causal, rows=rows, heads=[h])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(done * flop_per_head / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {w.H_q} q heads x every 4th query row ({rows.size} rows) of the "
+                  f"T=8192 causal GQA prefill, float64 three-stage oracle, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one half of the step (for profiling runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards over (batch, kv head) with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from transformer_scaled_dot_flash_amd import attn as abi
+    from transformer_scaled_dot_flash_amd.workloads import DECODE_HEADLINE as wd
+    from transformer_scaled_dot_flash_amd.workloads import PREFILL_HEADLINE as wp
+
+    abi.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    log("generating inputs")
+    qp, kp, vp = (to_dev(x) for x in wp.make_inputs())
+    op = torch.empty_like(qp)
+    qd, kd, vd = (to_dev(x) for x in wd.make_inputs())
+    od = torch.empty_like(qd)
+    ws_bytes = abi.attn_fwd_decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.T_kv, wd.D, abi.ATTN_BF16, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    n_splits = abi.attn_fwd_decode_default_splits(wd.B, wd.H_q, wd.H_kv, wd.T_kv, wd.D)
+    torch.cuda.synchronize()
+
+    do_p = args.only in (None, "prefill")
+    do_d = args.only in (None, "decode")
+
+    def run_prefill():
+        abi.attn_fwd_prefill(qp, kp, vp, op, wp.B, wp.H_q, wp.H_kv, wp.T_q, wp.T_kv, wp.D, wp.causal,
+                             wp.scale, abi.ATTN_BF16, stream)
+
+    def run_decode():
+        abi.attn_fwd_decode(qd, kd, vd, od, wd.B, wd.H_q, wd.H_kv, 1, wd.T_kv, wd.D, False, wd.scale,
+                            abi.ATTN_BF16, 0, ws, ws_bytes, stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        if do_p:
+            run_prefill()
+        if do_d:
+            run_decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        if do_p:
+            run_prefill()
+        e[1].record(stream)
+        e[2].record(stream)
+        if do_d:
+            run_decode()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region done")
+
+    p_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    d_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    p_avg = sum(p_ms) / K
+    d_avg = sum(d_ms) / K
+    p_tflops = wp.flops() / (p_avg * 1e-3) / 1e12 if do_p else None
+    d_gbs = wd.bytes() / (d_avg * 1e-3) / 1e9 if do_d else None
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read + {n} bytes written")
+
+    csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
+    prefill_digest = source_digest([csrc / "prefill_bf16.hip", csrc / "kernel_common.h"])
+    decode_digest = source_digest([csrc / "decode_bf16.hip", csrc / "kernel_common.h"])
+
+    result = {
+        "metric": METRIC,
+        "value": round(p_tflops, 3) if p_tflops else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill: causal GQA B=1 H_q=32 H_kv=8 T=8192 D=128 bf16 (scale 1/sqrt(128)); "
+                        "decode: B=64 H_q=32 H_kv=8 T_q=1 T_kv=4096 D=128 bf16",
+            "prefill_flops": wp.flops(),
+            "decode_bytes": wd.bytes(),
+            "decode_splits": n_splits,
+            "inputs": "i.i.d. N(0,1), seeded SplitMix64 + Box-Muller, rounded to bf16",
+        },
+    }
+    if do_p:
+        result["roofline"] = {
+            "bound": "mfma",
+            "kernel": "prefill_bf16_kernel<128,64,causal>",
+            "achieved": round(p_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profile("prefill_bf16_T8192_D128_gqa", prefill_digest),
+            "avg_launch_us": round(p_avg * 1e3, 2),
+            "min_launch_us": round(min(p_ms) * 1e3, 2),
+        }
+    if do_d:
+        result["decode"] = {
+            "metric": "decode KV-read GB/s",
+            "value": round(d_gbs, 1),
+            "unit": "GB/s",
+            "roofline": {
+                "bound": "hbm",
+                "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                "achieved": round(d_gbs, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(d_gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic_from_profile("decode_bf16_B64_T4096_D128", decode_digest),
+                "avg_call_us": round(d_avg * 1e3, 2),
+                "min_call_us": round(min(d_ms) * 1e3, 2),
+            },
+        }
+    if not args.no_cpu_baseline and do_p:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+/*
+ * attn.h - C ABI of the scaled dot-product attention forward for AMD MI355X
+ * (gfx950).
+ *
+ * The operation (learn-cuda-from-scratch Ch. 11 "Attention", section 11.1;
+ * AIInfraGuide "3.3 Self-Attention机制深入理解", sections 3.2-3.6):
+ *
+ *     O[b, h, i, :] = sum_j P[i, j] * V[b, g, j, :]
+ *     P[i, :]       = softmax_j( scale * sum_d Q[b, h, i, d] * K[b, g, j, d]  + mask[i, j] )
+ *     g             = h / (H_q / H_kv)
+ *
+ * mask[i, j] is 0 where key j is visible to query row i and -inf elsewhere.
+ * Non-causal: every key is visible.  Causal (Ch. 11 page, section 11.1:
+ * token i may not see j > i): row i sits at absolute position
+ * i + (T_kv - T_q) and sees keys j <= i + (T_kv - T_q).  With T_q == T_kv
+ * this is the usual j <= i; with T_q < T_kv it is a chunk of queries placed
+ * at the end of the keys; with T_q == 1 (decode) every key is visible.
+ *
+ * The head mapping covers MHA (H_kv == H_q), MQA (H_kv == 1) and GQA
+ * (anything that divides H_q): consecutive query heads share one kv head
+ * (Ch. 11 page, sections 11.8.1 and 11.11; AIInfraGuide page, section 9.3).
+ *
+ * Layout (no strides): Q and O are contiguous row-major [B][H_q][T_q][D];
+ * K and V are contiguous row-major [B][H_kv][T_kv][D].  All four tensors
+ * have the element type `dtype`.  Pointers are device pointers, 16-byte
+ * aligned; O must not overlap Q, K or V.
+ *
+ * Arithmetic: bf16 tensors are multiplied on bf16 matrix cores with fp32
+ * accumulation, the softmax runs in fp32, the weights are rounded to bf16
+ * for the P*V product and O is rounded once to bf16 (round-to-nearest-even).
+ * fp32 tensors use fp32 arithmetic throughout.  The T_q x T_kv score and
+ * weight matrices are never written to memory.
+ *
+ * Ownership and asynchrony: the caller owns every buffer, including the
+ * decode workspace; the library keeps no pointer after a call returns and
+ * allocates no device memory.  Calls only enqueue work on `stream` (a
+ * hipStream_t; NULL is the null stream) and never synchronise.  Launch
+ * failures return ATTN_ERR_HIP (attn_last_hip_error() gives the HIP code
+ * of the calling thread's last failure); faults inside a kernel surface at
+ * the caller's next synchronisation.
+ *
+ * Validation: every argument check runs on the host before any HIP call,
+ * in this order: shape and parameter values, empty problem, null pointers,
+ * alignment, aliasing, workspace.  B == 0 or T_q == 0 is an empty problem:
+ * the call returns ATTN_OK, launches nothing and ignores the pointers.
+ *
+ * Thread safety: all functions are re-entrant; the library holds no mutable
+ * state except the per-thread last HIP error.  Results are bitwise
+ * deterministic for fixed arguments (including the decode split count).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_PTR = 1,       /* a tensor pointer (or workspace) is NULL   */
+    ATTN_ERR_INVALID_SHAPE = 2,  /* negative size, H <= 0, H_q % H_kv != 0,   */
+                                 /* T_kv <= 0, causal with T_q > T_kv, or a   */
+                                 /* size too large for the launch grid        */
+    ATTN_ERR_UNSUPPORTED = 3,    /* D not 64 or 128; unknown dtype; decode    */
+                                 /* with T_q != 1; split count out of range   */
+    ATTN_ERR_INVALID_SCALE = 4,  /* scale is NaN or infinite                  */
+    ATTN_ERR_ALIGNMENT = 5,      /* a pointer is not 16-byte aligned          */
+    ATTN_ERR_ALIAS = 6,          /* O overlaps Q, K or V (or the workspace)   */
+    ATTN_ERR_WORKSPACE = 7,      /* decode workspace too small                */
+    ATTN_ERR_HIP = 8             /* a HIP launch call failed                  */
+} attn_status_t;
+
+typedef enum attn_dtype {
+    ATTN_F32 = 0,   /* IEEE binary32 */
+    ATTN_BF16 = 1   /* bfloat16      */
+} attn_dtype_t;
+
+/*
+ * Prefill / general forward: any T_q >= 0, T_kv >= 1 (causal needs
+ * T_q <= T_kv).  One kernel launch.  bf16: tiled over (query tile, q head,
+ * batch) with online softmax (AIInfraGuide page, sections 7.3, 12.2 and
+ * 12.3); key tiles wholly above the causal diagonal are skipped and only
+ * tiles that cross it are masked element by element (Ch. 11 page, section
+ * 11.8.3).  fp32: same math with fp32 FMA instead of matrix cores.
+ *
+ *   q, k, v  device input tensors (layout above), read only
+ *   o        device output tensor, fully overwritten
+ *   scale    multiplier of the raw dot product (e.g. 1/sqrt(D)); any finite
+ *            value
+ *   causal   0 or nonzero
+ *   dtype    ATTN_F32 or ATTN_BF16
+ *   stream   hipStream_t to enqueue on
+ */
+attn_status_t attn_fwd_prefill(const void* q, const void* k, const void* v, void* o,
+                               int B, int H_q, int H_kv, int T_q, int T_kv, int D,
+                               int causal, float scale, int dtype, void* stream);
+
+/*
+ * Decode forward: one query token per (batch, q head) against T_kv cached
+ * keys (Ch. 11 page, section 11.8.2: decode is a vector against the whole
+ * KV cache and is memory-bound).  T_q must be 1; `causal` is accepted and
+ * has no effect (the single row sees every key).
+ *
+ * bf16: the keys are cut into `num_splits` contiguous ranges; one pass
+ * writes a partial (running max, exponential sum, unnormalised output) per
+ * (batch, q head, split) into `workspace`, a second pass merges them with
+ * the block-merge rule of AIInfraGuide section 12.3 and writes O.  Each
+ * kv head's keys and values are read once for all of its query heads.
+ * fp32: one pass, no workspace used (workspace may be NULL).
+ *
+ *   num_splits       0 = library default (attn_fwd_decode_default_splits),
+ *                    else 1..1024; clamped to the number of 32-key blocks.
+ *   workspace        device buffer of at least
+ *                    attn_fwd_decode_workspace_bytes(...) bytes, 16-byte
+ *                    aligned, not overlapping O; contents on entry are
+ *                    ignored and on exit unspecified.
+ */
+attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void* o,
+                              int B, int H_q, int H_kv, int T_q, int T_kv, int D,
+                              int causal, float scale, int dtype, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_decode needs for these sizes (num_splits as
+ * passed to attn_fwd_decode, 0 = default).  Returns 0 for invalid sizes and
+ * for dtype ATTN_F32. */
+size_t attn_fwd_decode_workspace_bytes(int B, int H_q, int H_kv, int T_kv, int D,
+                                       int dtype, int num_splits);
+
+/* Split count attn_fwd_decode uses when num_splits == 0 (>= 1; 0 for
+ * invalid sizes). */
+int attn_fwd_decode_default_splits(int B, int H_q, int H_kv, int T_kv, int D);
+
+/* Static, NUL-terminated description of a status code. */
+const char* attn_status_string(int status);
+
+/* ATTN_ABI_VERSION of the library. */
+int attn_abi_version(void);
+
+/* HIP error code (hipError_t) of the calling thread's last ATTN_ERR_HIP. */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,229 @@
+// C ABI of the attention forward: argument checks and dispatch.
+// Every check runs on the host before any HIP call, so all error paths can
+// be exercised without a GPU.  The contract is documented in include/attn.h.
+#include <math.h>
+
+#include "attn.h"
+#include "kernel_common.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxSplits = 1024;
+constexpr int kDecodeBlock = 32;  // keys per decode tile; splits are multiples of it
+
+size_t elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Shape / parameter checks shared by both entry points.
+attn_status_t check_params(int B, int H_q, int H_kv, int T_q, int T_kv, int D, int dtype,
+                           float scale) {
+    if (B < 0 || T_q < 0 || H_q <= 0 || H_kv <= 0 || T_kv <= 0) return ATTN_ERR_INVALID_SHAPE;
+    if (H_q % H_kv != 0) return ATTN_ERR_INVALID_SHAPE;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_SCALE;
+    // One (batch, head) slice of any tensor must stay below 2 GiB: kernels
+    // address it with 32-bit offsets.
+    const long long es = (long long)elem_size(dtype);
+    if ((long long)T_q * D * es >= (1LL << 31) || (long long)T_kv * D * es >= (1LL << 31))
+        return ATTN_ERR_INVALID_SHAPE;
+    return ATTN_OK;
+}
+
+attn_status_t check_tensors(const void* q, const void* k, const void* v, const void* o, int B,
+                            int H_q, int H_kv, int T_q, int T_kv, int D, int dtype) {
+    if (!q || !k || !v || !o) return ATTN_ERR_NULL_PTR;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return ATTN_ERR_ALIGNMENT;
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)B * H_q * T_q * D * es;
+    const size_t nkv = (size_t)B * H_kv * T_kv * D * es;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+attn_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+}
+
+float log2_scale(float scale) { return (float)((double)scale * attn::kLog2e); }
+
+struct SplitPlan {
+    int n_splits;
+    int keys_per_split;
+};
+
+int default_splits(int B, int H_q, int H_kv, int T_kv) {
+    const int G = H_q / H_kv;
+    const long long groups = (long long)B * H_kv * ((G + 31) / 32);
+    const int n_blocks = (T_kv + kDecodeBlock - 1) / kDecodeBlock;
+    // Aim for about 4096 waves in flight (16 per CU); keep >= 4 tiles per split.
+    long long want = (4096 + groups - 1) / groups;
+    long long cap = n_blocks / 4;
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    if (want > kMaxSplits) want = kMaxSplits;
+    if (want < 1) want = 1;
+    return (int)want;
+}
+
+SplitPlan plan_splits(int B, int H_q, int H_kv, int T_kv, int requested) {
+    const int n_blocks = (T_kv + kDecodeBlock - 1) / kDecodeBlock;
+    int n = requested > 0 ? requested : default_splits(B, H_q, H_kv, T_kv);
+    if (n > n_blocks) n = n_blocks;
+    const int blocks_per = (n_blocks + n - 1) / n;
+    SplitPlan p;
+    p.keys_per_split = blocks_per * kDecodeBlock;
+    p.n_splits = (T_kv + p.keys_per_split - 1) / p.keys_per_split;  // no empty split
+    return p;
+}
+
+size_t decode_ws_bytes(int B, int H_q, int D, const SplitPlan& p) {
+    return (size_t)B * H_q * p.n_splits * (D + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_prefill(const void* q, const void* k, const void* v, void* o, int B,
+                               int H_q, int H_kv, int T_q, int T_kv, int D, int causal,
+                               float scale, int dtype, void* stream) {
+    attn_status_t st = check_params(B, H_q, H_kv, T_q, T_kv, D, dtype, scale);
+    if (st != ATTN_OK) return st;
+    if (causal && T_q > T_kv) return ATTN_ERR_INVALID_SHAPE;
+    // Grid limits: bf16 launches B*H_q*ceil(T_q/128) workgroups, fp32
+    // B*H_kv*ceil(G*T_q/64); both must fit a 32-bit grid dimension.
+    const long long G = H_q / H_kv;
+    const long long g_bf16 = (long long)B * H_q * ((T_q + 127) / 128);
+    const long long g_f32 = (long long)B * H_kv * ((G * T_q + 63) / 64);
+    if (g_bf16 > 0x7fffffffLL || g_f32 > 0x7fffffffLL) return ATTN_ERR_INVALID_SHAPE;
+    if (B == 0 || T_q == 0) return ATTN_OK;  // empty problem
+    st = check_tensors(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, dtype);
+    if (st != ATTN_OK) return st;
+
+    attn::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.T_q = T_q;
+    a.T_kv = T_kv;
+    a.D = D;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    a.scale_log2 = log2_scale(scale);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, s)
+                                         : attn::launch_prefill_f32(a, s));
+}
+
+attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void* o, int B,
+                              int H_q, int H_kv, int T_q, int T_kv, int D, int causal,
+                              float scale, int dtype, int num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    attn_status_t st = check_params(B, H_q, H_kv, T_q, T_kv, D, dtype, scale);
+    if (st != ATTN_OK) return st;
+    if (T_q != 1) return ATTN_ERR_UNSUPPORTED;
+    if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_UNSUPPORTED;
+    const long long waves = (long long)B * H_kv * ((H_q / H_kv + 31) / 32) * kMaxSplits;
+    if (waves / 4 > 0x7fffffffLL || (long long)B * H_q > 0x7fffffffLL) return ATTN_ERR_INVALID_SHAPE;
+    (void)causal;  // one query row at the end of the keys sees every key
+    if (B == 0) return ATTN_OK;
+    st = check_tensors(q, k, v, o, B, H_q, H_kv, 1, T_kv, D, dtype);
+    if (st != ATTN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (dtype == ATTN_F32) {
+        attn::PrefillArgs a;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.o = o;
+        a.B = B;
+        a.H_q = H_q;
+        a.H_kv = H_kv;
+        a.T_q = 1;
+        a.T_kv = T_kv;
+        a.D = D;
+        a.causal = 0;
+        a.scale = scale;
+        a.scale_log2 = log2_scale(scale);
+        return hip_status(attn::launch_prefill_f32(a, s));
+    }
+
+    const SplitPlan p = plan_splits(B, H_q, H_kv, T_kv, num_splits);
+    const size_t need = decode_ws_bytes(B, H_q, D, p);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (misaligned(workspace)) return ATTN_ERR_ALIGNMENT;
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)B * H_q * D * es;
+    const size_t nkv = (size_t)B * H_kv * T_kv * D * es;
+    if (overlaps(workspace, need, o, nq) || overlaps(workspace, need, q, nq) ||
+        overlaps(workspace, need, k, nkv) || overlaps(workspace, need, v, nkv))
+        return ATTN_ERR_ALIAS;
+
+    attn::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.T_kv = T_kv;
+    a.D = D;
+    a.scale_log2 = log2_scale(scale);
+    a.n_splits = p.n_splits;
+    a.keys_per_split = p.keys_per_split;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_o + (size_t)B * H_q * p.n_splits * D;
+    return hip_status(attn::launch_decode_bf16(a, s));
+}
+
+size_t attn_fwd_decode_workspace_bytes(int B, int H_q, int H_kv, int T_kv, int D, int dtype,
+                                       int num_splits) {
+    if (check_params(B, H_q, H_kv, 1, T_kv, D, dtype, 1.0f) != ATTN_OK) return 0;
+    if (num_splits < 0 || num_splits > kMaxSplits) return 0;
+    if (dtype == ATTN_F32) return 0;
+    return decode_ws_bytes(B, H_q, D, plan_splits(B, H_q, H_kv, T_kv, num_splits));
+}
+
+int attn_fwd_decode_default_splits(int B, int H_q, int H_kv, int T_kv, int D) {
+    if (check_params(B, H_q, H_kv, 1, T_kv, D, ATTN_BF16, 1.0f) != ATTN_OK) return 0;
+    return plan_splits(B, H_q, H_kv, T_kv, 0).n_splits;
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL_PTR: return "null pointer";
+        case ATTN_ERR_INVALID_SHAPE: return "invalid shape";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_ERR_INVALID_SCALE: return "scale is not finite";
+        case ATTN_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+        case ATTN_ERR_ALIAS: return "output overlaps an input or the workspace";
+        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

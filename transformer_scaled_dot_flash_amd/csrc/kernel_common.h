@@ -1,0 +1,90 @@
+// Internal declarations shared by the HIP kernels and the C ABI layer.
+// gfx950 (CDNA4) only: wave64, bf16 MFMA, 160 KiB LDS per workgroup.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resources: 32-bit offsets from an SGPR base, and hardware range
+// checking (loads past `num_bytes` return 0, stores past it are dropped).
+// Every tensor slice a kernel addresses through one is < 2 GiB (checked on
+// the host).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                             0x00020000);
+}
+__device__ inline u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+__device__ inline void buf_store_b64(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte_off, 0, 0);
+}
+__device__ inline void buf_store_b128(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, 0);
+}
+
+// log2(e): the kernels evaluate exp(x) as exp2(x * log2 e) and fold the
+// factor into the score multiplier once on the host.
+constexpr double kLog2e = 1.4426950408889634073599246810019;
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int B, H_q, H_kv, T_q, T_kv, D;
+    int causal;
+    float scale;       // multiplier of the raw dot product
+    float scale_log2;  // scale * log2(e), rounded to float
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int B, H_q, H_kv, T_kv, D;
+    float scale_log2;
+    int n_splits;        // effective split count (no split is empty)
+    int keys_per_split;  // multiple of 32
+    float* ws_o;         // [B][H_q][n_splits][D]  unnormalised partial outputs
+    float* ws_ml;        // [B][H_q][n_splits][2]  (running max in log2 units, sum)
+};
+
+// Launchers return the HIP status of the launch call itself.
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+template <typename Tup, size_t... I>
+inline void fill_ptrs(Tup& t, void** p, std::index_sequence<I...>) {
+    ((p[I] = static_cast<void*>(&std::get<I>(t))), ...);
+}
+
+// Launch a kernel and return the launch's own error code (no reliance on the
+// thread's sticky last-error state).
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                                hipStream_t s, Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
+    auto tup = std::make_tuple(static_cast<KArgs>(args)...);
+    void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    fill_ptrs(tup, ptrs, std::index_sequence_for<KArgs...>{});
+    return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, s);
+}
+
+}  // namespace attn

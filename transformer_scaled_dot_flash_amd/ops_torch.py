@@ -1,0 +1,68 @@
+"""torch front end: allocate outputs/workspace with torch and call the C ABI.
+
+Device memory and streams come from PyTorch; the computation is the HIP
+library's.  Tensors must be contiguous [B][H][T][D] on one GPU, all of the
+same dtype (torch.bfloat16 or torch.float32).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import attn as _abi
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _abi.ATTN_BF16
+    if t.dtype == torch.float32:
+        return _abi.ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B][H][T][D]")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B][H][T][D]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+
+
+def prefill(q, k, v, causal: bool, scale: float, out=None, stream=None):
+    """O = softmax(scale * Q K^T + mask) V; returns ``out`` (allocated if None)."""
+    _check(q, k, v)
+    B, H_q, T_q, D = q.shape
+    _, H_kv, T_kv, _ = k.shape
+    o = torch.empty_like(q) if out is None else out
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    _abi.attn_fwd_prefill(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, causal, scale, _dtype_code(q), s)
+    return o
+
+
+def decode_workspace(q, k, num_splits: int = 0):
+    """Workspace tensor (uint8) sized for a decode call, or None if not needed."""
+    B, H_q, _, D = q.shape
+    _, H_kv, T_kv, _ = k.shape
+    n = _abi.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, _dtype_code(q), num_splits)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def decode(q, k, v, scale: float, num_splits: int = 0, workspace=None, out=None, stream=None):
+    """One query token per (batch, q head) against T_kv keys; q is [B][H_q][1][D]."""
+    _check(q, k, v)
+    B, H_q, T_q, D = q.shape
+    _, H_kv, T_kv, _ = k.shape
+    o = torch.empty_like(q) if out is None else out
+    ws = decode_workspace(q, k, num_splits) if workspace is None else workspace
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    _abi.attn_fwd_decode(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, False, scale, _dtype_code(q),
+                         num_splits, ws, ws_bytes, s)
+    return o
