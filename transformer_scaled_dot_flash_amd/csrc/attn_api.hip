@@ -1,6 +1,7 @@
 // C ABI of the attention forward: argument checks and dispatch.
 // Every check runs on the host before any HIP call, so all error paths can
 // be exercised without a GPU.  The contract is documented in include/attn.h.
+#include <float.h>
 #include <math.h>
 
 #include "attn.h"
@@ -57,6 +58,18 @@ attn_status_t hip_status(hipError_t e) {
 }
 
 float log2_scale(float scale) { return (float)((double)scale * attn::kLog2e); }
+
+// The bf16 kernels take a positive multiplier: a negative scale is applied
+// by negating Q (exact), and a zero scale by the smallest normal float, which
+// gives bitwise the same weights (every exponent rounds to 2^0).
+void positive_scale(float scale, float* c, int* neg) {
+    double v = (double)scale * attn::kLog2e;
+    *neg = v < 0 ? 1 : 0;
+    v = v < 0 ? -v : v;
+    float f = (float)v;
+    if (!(f >= FLT_MIN)) f = FLT_MIN;
+    *c = f;
+}
 
 struct SplitPlan {
     int n_splits;
@@ -126,6 +139,7 @@ attn_status_t attn_fwd_prefill(const void* q, const void* k, const void* v, void
     a.causal = causal ? 1 : 0;
     a.scale = scale;
     a.scale_log2 = log2_scale(scale);
+    positive_scale(scale, &a.c_log2, &a.neg_q);
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, s)
                                          : attn::launch_prefill_f32(a, s));
@@ -162,6 +176,7 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
         a.causal = 0;
         a.scale = scale;
         a.scale_log2 = log2_scale(scale);
+        positive_scale(scale, &a.c_log2, &a.neg_q);
         return hip_status(attn::launch_prefill_f32(a, s));
     }
 

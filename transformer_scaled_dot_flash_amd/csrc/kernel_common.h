@@ -18,6 +18,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // Raw buffer resources: 32-bit offsets from an SGPR base, and hardware range
 // checking (loads past `num_bytes` return 0, stores past it are dropped).
@@ -30,6 +33,22 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nu
 __device__ inline u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
+// 16-byte load from a buffer straight into LDS: lane i's 16 bytes land at
+// lds_block + 16 * i (lds_block is wave-uniform).  Out-of-range lanes write
+// zeros.
+__device__ inline void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_block, uint32_t byte_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 16, (int)byte_off, 0, 0, 0);
+}
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// source lane r points at 4 consecutive bf16 values R[r][0..3]; destination
+// lane i receives R[i/4 + 4k][i%4] for k = 0..3.
+__device__ inline bf16x4 lds_read_tr16(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+// Wait until this wave has no vector-memory operation in flight (vmcnt = 0),
+// leaving the LDS/scalar and export counters unconstrained.
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 __device__ inline void buf_store_b64(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte_off, 0, 0);
 }
@@ -50,6 +69,8 @@ struct PrefillArgs {
     int causal;
     float scale;       // multiplier of the raw dot product
     float scale_log2;  // scale * log2(e), rounded to float
+    float c_log2;      // |scale| * log2(e), >= FLT_MIN (0 becomes FLT_MIN: same weights)
+    int neg_q;         // 1 when scale < 0: the kernels flip Q's sign instead
 };
 
 struct DecodeArgs {

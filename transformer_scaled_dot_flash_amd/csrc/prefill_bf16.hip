@@ -9,25 +9,34 @@
 // leave the chip.
 //
 // gfx950 mapping:
-//   * 4 waves x 32 query rows.  Each wave computes S^T = K * Q^T for 32 keys
-//     at a time with v_mfma_f32_32x32x16_bf16, so the accumulator layout puts
-//     one query row in each lane column and 16 keys in each lane: the row
-//     maximum and row sum are in-lane, plus a single exchange with lane^32.
-//   * The same layout is the B operand of O^T = V^T * P^T: the weights are
-//     converted to bf16 in place and never move between lanes.  V is stored
-//     transposed in LDS (key-contiguous per feature) so the A operand of the
-//     P*V product is two 8-byte LDS reads per lane.
-//   * K and V tiles come from HBM with 16-byte loads, each row of a tile read
-//     contiguously, and are double-buffered in LDS: the next tile is in
-//     flight in registers while the current one is consumed.  XOR swizzles
-//     keep the LDS reads and writes free of bank conflicts without padding.
+//   * 4 waves x 32 query rows, two workgroups per CU (<= 256 registers per
+//     lane), so one wave's softmax overlaps the other's matrix work.
+//   * Each wave computes S^T = K * Q^T for 32 keys at a time with
+//     v_mfma_f32_32x32x16_bf16: one query row per lane column and 16 keys per
+//     lane, so the row maximum is in-lane plus one exchange with lane^32.
+//   * The same layout is the B operand of O^T = V^T * P^T: weights are
+//     rounded to bf16 in place and never move between lanes.  The V^T A
+//     operand comes straight from the row-major V tile with the transposing
+//     LDS read ds_read_b64_tr_b16.
+//   * K and V tiles go from HBM to LDS with 16-byte buffer loads that write
+//     LDS directly (no register staging), double-buffered: the next tile is
+//     in flight while the current one is consumed.  Each 1 KiB load covers
+//     whole rows; an XOR swizzle of the 16-byte chunks (chosen through the
+//     per-lane source address) keeps both the K reads and the transposing V
+//     reads free of bank conflicts.
+//   * Softmax in the exp2 domain: the row maximum is taken on raw scores,
+//     one FMA forms score * scale * log2(e) - max, and the maximum used for
+//     the exponent is only moved when a row's maximum grows by more than 8
+//     (so weights stay <= 2^8 and the O rescale is rare; the final O / l is
+//     the same for any base).  Row sums add the bf16-rounded weights with
+//     v_dot2_f32_bf16, so O stays a convex combination of V's rows.
 //   * Causal: key tiles wholly above the diagonal are never visited (per
 //     workgroup) or skipped (per wave); only tiles that cross the diagonal or
 //     the end of the keys pay for the element mask (Ch. 11 "Attention" page,
 //     section 11.8.3), using exact tile bounds.
-//   * Workgroups are ordered heaviest query tile first (causal work grows
-//     along the sequence) and, when the kv-head count allows, all workgroups
-//     of one kv head are placed on one XCD so its K/V stay in that XCD's L2.
+//   * Workgroups run heaviest query tile first (causal work grows along the
+//     sequence) and, when the kv-head count allows, all workgroups of one kv
+//     head run on one XCD so its K/V stay in that XCD's L2.
 #include "kernel_common.h"
 
 namespace attn {
@@ -36,6 +45,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per tile
+constexpr int kStages = 2;
 
 struct TileCoord {
     int qt, b, hq, hk;
@@ -73,26 +84,27 @@ __device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt,
     return t;
 }
 
-// Transposed-V swizzle: feature row d stores its 4-key group g at g ^ vswz(d).
-__device__ inline int vswz(int d) { return (d ^ (d >> 3)) & 15; }
+// 16-byte chunk c of tile row `key` is stored at chunk c ^ swz(key).  Any 16
+// consecutive keys (8 for D = 64) map to distinct chunks, and 4 consecutive
+// keys aligned to 4 keep two adjacent chunks apart, which is what the K reads
+// and the transposing V reads need.
+template <int CPR>
+__device__ inline int swz(int key) {
+    return (((key & 3) << 1) | ((key >> 2) & 1) | (key & 8)) & (CPR - 1);
+}
 
-__device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                    const bf16* __restrict__ V, bf16* __restrict__ O, int B, int H_q, int H_kv,
+                    int T_q, int T_kv, int n_qt, float c, int neg_q) {
+    constexpr int CPR = D / 8;                    // 16-byte chunks per row
+    constexpr int ROWB = D * 2;                   // bytes per row
+    constexpr int TILE = kBN * ROWB;              // bytes of one K or V tile
+    constexpr int NLD = TILE / (1024 * kWaves);   // 1 KiB loads per wave per tile and operand
+    static_assert(NLD * 1024 * kWaves == TILE, "tile must split into 1 KiB wave loads");
 
-template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, int B, int H_q, int H_kv, int T_q, int T_kv, int n_qt, float scale_log2) {
-    constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int KSW = CPR - 1;        // K chunk swizzle mask
-    constexpr int STAGE = 2 * BN * D;   // bf16 elements per LDS stage (K + V^T)
-    constexpr int NK = BN * CPR / kThreads;
-    constexpr int NVQ = (BN / 4) * CPR / kThreads;
-    static_assert(NK * kThreads == BN * CPR, "K tile must split evenly over threads");
-    static_assert(NVQ * kThreads == (BN / 4) * CPR, "V tile must split evenly over threads");
-    static_assert(BN % 32 == 0 && BN / 4 >= 16, "key tile");
-
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * 2 * TILE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -101,8 +113,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     const int hi = lane >> 5;
 
     const TileCoord tc = map_tile(blockIdx.x, B, H_q, H_kv, n_qt, CAUSAL);
-    const uint32_t q_bytes = (uint32_t)T_q * D * 2;
-    const uint32_t kv_bytes = (uint32_t)T_kv * D * 2;
+    const uint32_t q_bytes = (uint32_t)T_q * ROWB;
+    const uint32_t kv_bytes = (uint32_t)T_kv * ROWB;
     const auto rQ = make_rsrc(Q + (size_t)(tc.b * H_q + tc.hq) * T_q * D, q_bytes);
     const auto rK = make_rsrc(K + (size_t)(tc.b * H_kv + tc.hk) * T_kv * D, kv_bytes);
     const auto rV = make_rsrc(V + (size_t)(tc.b * H_kv + tc.hk) * T_kv * D, kv_bytes);
@@ -113,170 +125,153 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     const int row0 = q0 + wave * 32;
     const int my_row = row0 + l32;
 
-    // Q fragment: B operand of S^T = K Q^T (column = query row, 8 features).
-    // Rows past T_q read as zero (buffer range check).
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8, buf_load_b128(rQ, (uint32_t)(my_row * D + 16 * s + 8 * hi) * 2));
-
-    // Key ranges.
+    // Key ranges: the workgroup's and this wave's.
     const int last_row = min(T_q, q0 + kBM) - 1;
     const int kv_end = CAUSAL ? min(T_kv, last_row + off + 1) : T_kv;
-    const int n_kt = (kv_end + BN - 1) / BN;
+    const int n_kt = (kv_end + kBN - 1) / kBN;
     const int wave_last = min(T_q - 1, row0 + 31);
     const int wave_kv_end = (row0 >= T_q) ? 0 : (CAUSAL ? min(T_kv, wave_last + off + 1) : T_kv);
+    const int lim = CAUSAL ? min(T_kv - 1, my_row + off) : T_kv - 1;  // last visible key of my row
 
-    // Keys past T_kv read as zero (buffer range check) and are masked.
-    u32x4 kr[NK];
-    u32x4 vr[NVQ][4];
-
-    auto load_tile = [&](int j0) {
+    // Issue the direct-to-LDS loads of key tile t (K and V) into stage t % 2.
+    // Keys past T_kv are outside the buffer range and load as zero.
+    auto issue = [&](int t) {
+        unsigned char* kst = smem + (t % kStages) * 2 * TILE;
+        unsigned char* vst = kst + TILE;
+        const int j0 = t * kBN;
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c / CPR, ch = c % CPR;
-            kr[i] = buf_load_b128(rK, (uint32_t)((j0 + row) * D + ch * 8) * 2);
-        }
-#pragma unroll
-        for (int i = 0; i < NVQ; ++i) {
-            const int u = tid + i * kThreads;
-            const int ch = u % CPR, kq = u / CPR;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                vr[i][r] = buf_load_b128(rV, (uint32_t)((j0 + 4 * kq + r) * D + ch * 8) * 2);
+        for (int n = 0; n < NLD; ++n) {
+            const int blk = wave * NLD + n;
+            const int p = blk * 64 + lane;  // chunk slot in the tile
+            const int row = p / CPR;
+            const int logical = (p % CPR) ^ swz<CPR>(row);
+            const uint32_t boff = (uint32_t)(j0 + row) * ROWB + logical * 16;
+            buf_load_lds16(rK, kst + blk * 1024, boff);
+            buf_load_lds16(rV, vst + blk * 1024, boff);
         }
     };
 
-    auto store_tile = [&](int buf) {
-        bf16* ks = smem + buf * STAGE;
-        bf16* vt = ks + BN * D;
+    if (n_kt > 0) issue(0);
+
+    // Q fragment: B operand of S^T = K Q^T (column = query row, 8 features).
+    // Rows past T_q read as zero.  A negative scale is folded into Q's sign
+    // (exact in bf16), so c > 0 below.
+    bf16x8 qf[D / 16];
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c / CPR, ch = c % CPR;
-            *reinterpret_cast<u32x4*>(ks + row * D + ((ch ^ (row & KSW)) * 8)) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < NVQ; ++i) {
-            const int u = tid + i * kThreads;
-            const int ch = u % CPR, kq = u / CPR;
-            const u32x4 w0 = vr[i][0], w1 = vr[i][1], w2 = vr[i][2], w3 = vr[i][3];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // features ch*8 + 2w (low halves) and ch*8 + 2w + 1 (high halves)
-                const int d0 = ch * 8 + 2 * w;
-                const int d1 = d0 + 1;
-                const u32x2 lo = {pack_lo(w0[w], w1[w]), pack_lo(w2[w], w3[w])};
-                const u32x2 hi2 = {pack_hi(w0[w], w1[w]), pack_hi(w2[w], w3[w])};
-                *reinterpret_cast<u32x2*>(vt + d0 * BN + ((kq ^ vswz(d0)) * 4)) = lo;
-                *reinterpret_cast<u32x2*>(vt + d1 * BN + ((kq ^ vswz(d1)) * 4)) = hi2;
-            }
-        }
-    };
+    for (int s = 0; s < D / 16; ++s) {
+        u32x4 w = buf_load_b128(rQ, (uint32_t)(my_row * D + 16 * s + 8 * hi) * 2);
+        if (neg_q) w ^= 0x80008000u;
+        qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    float m_use = -INFINITY;  // base of the exponent (log2 units), per row
+    float l_run = 0.f;        // sum of bf16 weights relative to m_use (this lane's keys)
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-    if (n_kt > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
+    // Lane constants of the transposing V read.
+    const int tr_i = lane & 15;
+    const int tr_key = 4 * hi + (tr_i >> 2);                  // + 16 ks + 8 r
+    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);  // + 32 db
 
     for (int t = 0; t < n_kt; ++t) {
-        const int j0 = t * BN;
-        const bool has_next = t + 1 < n_kt;
-        if (has_next) load_tile(j0 + BN);
+        wait_vmem_all();  // this wave's part of tile t has landed
+        __syncthreads();  // ... and every other wave's; tile t-1 is no longer read
+        if (t + 1 < n_kt) issue(t + 1);
 
-        if (j0 < wave_kv_end) {
-            const bf16* ks = smem + (t & 1) * STAGE;
-            const bf16* vt = ks + BN * D;
+        const int j0 = t * kBN;
+        if (j0 >= wave_kv_end) continue;  // whole tile above this wave's diagonal
+        const unsigned char* kst = smem + (t % kStages) * 2 * TILE;
+        const unsigned char* vst = kst + TILE;
 
-            // S^T tile: rows = keys, columns = this wave's 32 query rows.
-            f32x16 sacc[BN / 32];
+        // S^T tile: rows = keys, columns = this wave's 32 query rows.
+        f32x16 sacc[kBN / 32];
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
-                sacc[kb] = f32x16{};
-                const int key = kb * 32 + l32;
-                const bf16* krow = ks + key * D;
+        for (int kb = 0; kb < kBN / 32; ++kb) {
+            sacc[kb] = f32x16{};
+            const int key = kb * 32 + l32;
+            const unsigned char* krow = kst + key * ROWB;
+            const int sw = swz<CPR>(key);
 #pragma unroll
-                for (int s = 0; s < D / 16; ++s) {
-                    const int ch = (2 * s + hi) ^ (key & KSW);
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ch * 8);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-                }
+            for (int s = 0; s < D / 16; ++s) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * s + hi) ^ sw) * 16));
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
             }
+        }
 
-            // Scale into log2 units, mask only where the tile needs it.
-            const bool need_mask = (j0 + BN > T_kv) || (CAUSAL && j0 + BN - 1 > row0 + off);
-            const int lim = CAUSAL ? min(T_kv - 1, my_row + off) : T_kv - 1;
-            float mx = -INFINITY;
+        // Mask (raw scores; c > 0) only where the tile needs it.
+        const bool need_mask = (j0 + kBN > T_kv) || (CAUSAL && j0 + kBN - 1 > row0 + off);
+        if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
+            for (int kb = 0; kb < kBN / 32; ++kb) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    float x = sacc[kb][j] * scale_log2;
-                    if (need_mask) {
-                        const int key = j0 + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-                        x = key <= lim ? x : -INFINITY;
-                    }
-                    sacc[kb][j] = x;
-                    mx = fmaxf(mx, x);
+                    const int key = j0 + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+                    sacc[kb][j] = key <= lim ? sacc[kb][j] : -INFINITY;
                 }
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
-
-            // Weights rounded to bf16 for the P*V product; the row sum uses
-            // the same rounded weights, so O stays a convex combination of
-            // the rows of V.
-            bf16x8 pb[BN / 16];
-            float psum = 0.f;
+        }
+        float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
+        for (int kb = 0; kb < kBN / 32; ++kb) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const bf16 p = (bf16)__builtin_amdgcn_exp2f(sacc[kb][j] - m_use);
-                    psum += (float)p;
-                    pb[kb * 2 + (j >> 3)][j & 7] = p;
-                }
-            }
-            l_run = l_run * alpha + psum;
+            for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sacc[kb][j], sacc[kb][j + 1]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = mx * c;  // -inf when the row sees no key of this tile
 
+        // Move the exponent base only when a row's maximum grew by more than 8.
+        if (__any(m_new > m_use + 8.f)) {
+            const float m_t = fmaxf(m_use, m_new);
+            const float alpha = (m_t == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_t);
+            l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
             }
+            m_use = m_t;
+        }
+        const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
 
-            // O^T += V^T P^T.  Lane (feature d, half hi) supplies V for keys
-            // 16ks + 4hi + {0..3} and 16ks + 8 + 4hi + {0..3}, the same keys
-            // its P operand holds.
+        // Weights, rounded to bf16 in place (the B operand of P*V), and their sum.
+        bf16x8 pb[kBN / 16];
+        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int d = db * 32 + l32;
-                const int sw = vswz(d);
-                const bf16* vrow = vt + d * BN;
+        for (int kb = 0; kb < kBN / 32; ++kb) {
 #pragma unroll
-                for (int ks2 = 0; ks2 < BN / 16; ++ks2) {
-                    const int g1 = 4 * ks2 + hi;
-                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + ((g1 ^ sw) * 4));
-                    const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vrow + (((g1 + 2) ^ sw) * 4));
-                    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks2], oacc[db], 0, 0, 0);
-                }
+            for (int j = 0; j < 16; j += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][j], c, -m_sub));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][j + 1], c, -m_sub));
+                const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
+                else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
+                pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
+                pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
             }
         }
+        l_run += ps0 + ps1;
 
-        if (has_next) store_tile((t + 1) & 1);
-        __syncthreads();
+        // O^T += V^T P^T.  Lane (feature d, half hi) needs V for keys
+        // 16ks + 4hi + {0..3} and 16ks + 8 + 4hi + {0..3}, the keys its P
+        // operand holds; two transposing reads deliver exactly those.
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int d = db * 32 + tr_d;
+            const int dchunk = d >> 3;
+            const int dbyte = (d & 7) * 2;
+#pragma unroll
+            for (int ks = 0; ks < kBN / 16; ++ks) {
+                const int k_lo = ks * 16 + tr_key;
+                const int k_hi = k_lo + 8;
+                const bf16x4 lo = lds_read_tr16(vst + k_lo * ROWB + ((dchunk ^ swz<CPR>(k_lo)) * 16) + dbyte);
+                const bf16x4 h4 = lds_read_tr16(vst + k_hi * ROWB + ((dchunk ^ swz<CPR>(k_hi)) * 16) + dbyte);
+                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
+            }
+        }
     }
 
     // Epilogue: O = O_acc / l, rounded once to bf16.  Rows past T_q fall
@@ -296,23 +291,21 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     }
 }
 
-template <int D, int BN, bool CAUSAL>
+template <int D, bool CAUSAL>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
     const int n_qt = (a.T_q + kBM - 1) / kBM;
     const long long grid = (long long)a.B * a.H_q * n_qt;
-    return launch_kernel(prefill_bf16_kernel<D, BN, CAUSAL>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+    return launch_kernel(prefill_bf16_kernel<D, CAUSAL>, dim3((unsigned)grid), dim3(kThreads), 0, s,
                          static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                          static_cast<const bf16*>(a.v), static_cast<bf16*>(a.o), a.B, a.H_q, a.H_kv,
-                         a.T_q, a.T_kv, n_qt, a.scale_log2);
+                         a.T_q, a.T_kv, n_qt, a.c_log2, a.neg_q);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-    if (a.D == 128) {
-        return a.causal ? launch_one<128, 64, true>(a, s) : launch_one<128, 64, false>(a, s);
-    }
-    return a.causal ? launch_one<64, 128, true>(a, s) : launch_one<64, 128, false>(a, s);
+    if (a.D == 128) return a.causal ? launch_one<128, true>(a, s) : launch_one<128, false>(a, s);
+    return a.causal ? launch_one<64, true>(a, s) : launch_one<64, false>(a, s);
 }
 
 }  // namespace attn
