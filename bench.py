@@ -4,7 +4,8 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   * prefill: Llama-3-8B-shaped causal GQA, B=1 H_q=32 H_kv=8 T=8192 D=128,
     bf16 (attn_fwd_prefill, one kernel);
   * decode:  B=64 H_q=32 H_kv=8, one query token against 4096 cached keys,
-    D=128, bf16 (attn_fwd_decode: split kernel + combine kernel).
+    D=128, bf16 (attn_fwd_decode; the 512 (batch, kv head) groups fill the
+    GPU, so one split kernel writes O and no combine pass runs).
 Inputs are seeded N(0,1) tensors, resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is the prefill throughput in TFLOP/s with
@@ -59,7 +60,7 @@ def traffic_from_profile(name, digest):
 
 def cpu_baseline(budget_s=15.0):
     """The CPU oracle, timed on this host on a bounded sample of the prefill
-    workload: q heads in order, every 4th query row, until the budget is
+    workload: q heads in order, every query row of each, until the budget is
     spent (at least one head)."""
     import numpy as np
     import oracle
@@ -72,7 +73,7 @@ def cpu_baseline(budget_s=15.0):
         threads = 1
     q, k, v = w.make_inputs()
     Q, K, V = (inputs.as_f64(x, w.dtype) for x in (q, k, v))
-    rows = np.arange(0, w.T_q, 4)
+    rows = np.arange(0, w.T_q)
     flop_per_head = sum(4 * w.D * (int(i) + 1) for i in rows)
     done = 0
     t0 = time.perf_counter()
@@ -87,7 +88,7 @@ def cpu_baseline(budget_s=15.0):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} of {w.H_q} q heads x every 4th query row ({rows.size} rows) of the "
+        "sample": f"{done} of {w.H_q} q heads x all {rows.size} query rows of the "
                   f"T=8192 causal GQA prefill, float64 three-stage oracle, {dt:.1f} s",
     }
 
@@ -95,8 +96,10 @@ def cpu_baseline(budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="minimum seconds of untimed warm-up (GPU clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time one half of the step (for profiling runs)")
@@ -145,12 +148,19 @@ def main():
         abi.attn_fwd_decode(qd, kd, vd, od, wd.B, wd.H_q, wd.H_kv, 1, wd.T_kv, wd.D, False, wd.scale,
                             abi.ATTN_BF16, 0, ws, ws_bytes, stream)
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
+    # Untimed warm-up: W steps, continued until the GPU clock has settled
+    # (at least --settle seconds of back-to-back work).
+    log(f"warmup {args.warmup} steps, >= {args.settle} s")
+    t_settle = time.perf_counter() + args.settle
+    done = 0
+    while done < args.warmup or time.perf_counter() < t_settle:
         if do_p:
             run_prefill()
         if do_d:
             run_decode()
+        done += 1
+        if done % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -233,7 +243,7 @@ def main():
             "unit": "GB/s",
             "roofline": {
                 "bound": "hbm",
-                "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                "kernel": "decode_split_kernel<128>" + (" + decode_combine_kernel<128>" if n_splits > 1 else ""),
                 "achieved": round(d_gbs, 1),
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",

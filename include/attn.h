@@ -108,16 +108,20 @@ attn_status_t attn_fwd_prefill(const void* q, const void* k, const void* v, void
  * bf16: the keys are cut into `num_splits` contiguous ranges; one pass
  * writes a partial (running max, exponential sum, unnormalised output) per
  * (batch, q head, split) into `workspace`, a second pass merges them with
- * the block-merge rule of AIInfraGuide section 12.3 and writes O.  Each
- * kv head's keys and values are read once for all of its query heads.
+ * the block-merge rule of AIInfraGuide section 12.3 and writes O (with one
+ * split the first pass writes O directly).  Each kv head's keys and values
+ * are read once for all of its query heads.
  * fp32: one pass, no workspace used (workspace may be NULL).
  *
  *   num_splits       0 = library default (attn_fwd_decode_default_splits),
  *                    else 1..1024; clamped to the number of 32-key blocks.
+ *                    With one split the split pass writes O itself and no
+ *                    workspace is needed.
  *   workspace        device buffer of at least
  *                    attn_fwd_decode_workspace_bytes(...) bytes, 16-byte
- *                    aligned, not overlapping O; contents on entry are
- *                    ignored and on exit unspecified.
+ *                    aligned, not overlapping O, Q, K or V; contents on
+ *                    entry are ignored and on exit unspecified.  May be NULL
+ *                    when that size is 0.
  */
 attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void* o,
                               int B, int H_q, int H_kv, int T_q, int T_kv, int D,
@@ -125,8 +129,8 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes attn_fwd_decode needs for these sizes (num_splits as
- * passed to attn_fwd_decode, 0 = default).  Returns 0 for invalid sizes and
- * for dtype ATTN_F32. */
+ * passed to attn_fwd_decode, 0 = default).  Returns 0 when no workspace is
+ * needed (one split, or dtype ATTN_F32) and for invalid sizes. */
 size_t attn_fwd_decode_workspace_bytes(int B, int H_q, int H_kv, int T_kv, int D,
                                        int dtype, int num_splits);
 

@@ -21,6 +21,12 @@ CSRC = PKG / "csrc"
 LIBDIR = PKG / "_lib"
 INCLUDE = ROOT / "include"
 
+# Kernel sources are compiled assuming no NaN operands (scores of finite
+# inputs are never NaN; masked scores are -inf), which lets max/min skip NaN
+# canonicalisation.  The ABI layer, which validates inputs, is not.
+KERNEL_FLAGS = ["-fno-honor-nans"]
+KERNEL_SOURCES = {"prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip"}
+
 HIP_SOURCES = [
     CSRC / "attn_api.hip",
     CSRC / "prefill_bf16.hip",
@@ -74,7 +80,8 @@ def build_hip(jobs: int = 4) -> Path:
     for src in HIP_SOURCES:
         obj = objdir / (src.stem + ".o")
         objs.append(obj)
-        cmd = [hipcc, *HIP_FLAGS, "-I", str(INCLUDE), "-I", str(CSRC), "-c", str(src), "-o", str(obj)]
+        extra = KERNEL_FLAGS if src.name in KERNEL_SOURCES else []
+        cmd = [hipcc, *HIP_FLAGS, *extra, "-I", str(INCLUDE), "-I", str(CSRC), "-c", str(src), "-o", str(obj)]
         print("[build]", " ".join(cmd), flush=True)
         procs.append(subprocess.Popen(cmd))
         if len(procs) >= jobs:

@@ -13,6 +13,7 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int kMaxSplits = 1024;
 constexpr int kDecodeBlock = 32;  // keys per decode tile; splits are multiples of it
+constexpr int kDecodeWaves = 512; // target decode waves (2 per CU)
 
 size_t elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
@@ -80,8 +81,10 @@ int default_splits(int B, int H_q, int H_kv, int T_kv) {
     const int G = H_q / H_kv;
     const long long groups = (long long)B * H_kv * ((G + 31) / 32);
     const int n_blocks = (T_kv + kDecodeBlock - 1) / kDecodeBlock;
-    // Aim for about 4096 waves in flight (16 per CU); keep >= 4 tiles per split.
-    long long want = (4096 + groups - 1) / groups;
+    // One wave per (group, split); about 512 waves (two per CU) stream the
+    // cache at full HBM rate.  Enough groups -> one split and no combine
+    // pass; fewer -> split the keys, keeping >= 4 tiles per split.
+    long long want = (kDecodeWaves + groups - 1) / groups;
     long long cap = n_blocks / 4;
     if (cap < 1) cap = 1;
     if (want > cap) want = cap;
@@ -102,6 +105,7 @@ SplitPlan plan_splits(int B, int H_q, int H_kv, int T_kv, int requested) {
 }
 
 size_t decode_ws_bytes(int B, int H_q, int D, const SplitPlan& p) {
+    if (p.n_splits == 1) return 0;  // the split pass writes O directly
     return (size_t)B * H_q * p.n_splits * (D + 2) * sizeof(float);
 }
 
@@ -182,8 +186,8 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
 
     const SplitPlan p = plan_splits(B, H_q, H_kv, T_kv, num_splits);
     const size_t need = decode_ws_bytes(B, H_q, D, p);
-    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    if (misaligned(workspace)) return ATTN_ERR_ALIGNMENT;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+    if (need > 0 && misaligned(workspace)) return ATTN_ERR_ALIGNMENT;
     const size_t es = elem_size(dtype);
     const size_t nq = (size_t)B * H_q * D * es;
     const size_t nkv = (size_t)B * H_kv * T_kv * D * es;
@@ -201,7 +205,7 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
     a.H_kv = H_kv;
     a.T_kv = T_kv;
     a.D = D;
-    a.scale_log2 = log2_scale(scale);
+    positive_scale(scale, &a.c_log2, &a.neg_q);
     a.n_splits = p.n_splits;
     a.keys_per_split = p.keys_per_split;
     a.ws_o = static_cast<float*>(workspace);

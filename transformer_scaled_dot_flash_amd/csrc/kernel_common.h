@@ -45,10 +45,40 @@ __device__ inline void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_block,
 __device__ inline bf16x4 lds_read_tr16(const void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
 }
-// Wait until this wave has no vector-memory operation in flight (vmcnt = 0),
-// leaving the LDS/scalar and export counters unconstrained.
-__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Wait until at most N vector-memory operations of this wave are in flight
+// (s_waitcnt vmcnt(N)), leaving the LDS/scalar and export counters
+// unconstrained.  gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14.
+template <int N>
+__device__ inline void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ inline void wait_vmem_all() { wait_vmem_le<0>(); }
 
+// Value of lane (lane ^ 32), through the LDS crossbar (no memory access).
+// `addr` = 4 * (lane ^ 32), computed once per kernel.
+__device__ inline float swap_halves(float x, int addr) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
+}
+
+// Layout of K and V tiles in LDS: row-major, 16-byte chunk c of row `key`
+// stored at chunk c ^ swz(key).  gfx950 LDS has 64 banks of 4 bytes (256 B
+// per clock).  The swizzle makes both read patterns conflict-free:
+//   * MFMA K reads, ds_read_b128 (16 lanes per clock): 16 consecutive keys,
+//     one logical chunk -> 16 distinct physical chunks;
+//   * transposing V reads, ds_read_b64_tr_b16 (32 lanes per clock): 4
+//     consecutive keys (aligned to 4) x 4 adjacent chunks -> 16 distinct
+//     bank groups.
+// With 256-byte rows (D = 128) every row starts at bank 0, so swz is a
+// bijection on 4 bits that moves the key's low 2 bits to the chunk's high
+// 2 bits.  With 128-byte rows (D = 64) odd rows start at bank 32, and the
+// 3-bit swizzle only has to separate keys of equal parity.
+template <int CPR>
+__device__ inline int swz(int key) {
+    if (CPR == 16) return ((key & 3) << 2) | ((key >> 2) & 3);
+    return (((key >> 1) & 1) << 2) | ((key >> 2) & 3);
+}
 __device__ inline void buf_store_b64(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte_off, 0, 0);
 }
@@ -79,7 +109,8 @@ struct DecodeArgs {
     const void* v;
     void* o;
     int B, H_q, H_kv, T_kv, D;
-    float scale_log2;
+    float c_log2;  // |scale| * log2(e), >= FLT_MIN
+    int neg_q;     // 1 when scale < 0 (Q's sign is flipped instead)
     int n_splits;        // effective split count (no split is empty)
     int keys_per_split;  // multiple of 32
     float* ws_o;         // [B][H_q][n_splits][D]  unnormalised partial outputs

@@ -42,18 +42,28 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-constexpr int kBN = 64;           // keys per tile
-constexpr int kStages = 2;
+#ifndef SCHED_HINTS
+#define SCHED_HINTS
+#endif
+
+// Tile configuration: keys per tile, waves (x 32 query rows) per workgroup,
+// depth of the LDS tile ring.
+#ifndef PF_BN
+#define PF_BN 64
+#endif
+#ifndef PF_WAVES
+#define PF_WAVES 4
+#endif
+#ifndef PF_STAGES
+#define PF_STAGES 3
+#endif
 
 struct TileCoord {
     int qt, b, hq, hk;
 };
 
 // Workgroup id -> (query tile, batch, q head, kv head).
-__device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt, bool causal) {
+__device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt, int BM, bool causal) {
     const int G = H_q / H_kv;
     const int units = B * H_kv;  // (batch, kv head) pairs
     int qt_rev, unit, g;
@@ -84,35 +94,62 @@ __device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt,
     return t;
 }
 
-// 16-byte chunk c of tile row `key` is stored at chunk c ^ swz(key).  Any 16
-// consecutive keys (8 for D = 64) map to distinct chunks, and 4 consecutive
-// keys aligned to 4 keep two adjacent chunks apart, which is what the K reads
-// and the transposing V reads need.
-template <int CPR>
-__device__ inline int swz(int key) {
-    return (((key & 3) << 1) | ((key >> 2) & 1) | (key & 8)) & (CPR - 1);
+// One key tile of S^T = K Q^T for this wave: kBN/32 independent MFMA chains
+// over the D/16 feature steps, interleaved.
+template <int D, int BN>
+struct STile {
+    f32x16 acc[BN / 32];
+};
+
+template <int D, int BN>
+__device__ inline void score_tile(STile<D, BN>& st, const unsigned char* kst, const bf16x8* qf,
+                                  int l32, int hi) {
+    constexpr int CPR = D / 8;
+    constexpr int ROWB = D * 2;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) st.acc[kb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            const int key = kb * 32 + l32;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                kst + key * ROWB + (((2 * s + hi) ^ swz<CPR>(key)) * 16));
+            st.acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st.acc[kb], 0, 0, 0);
+        }
+    }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+// Software pipeline per wave: while the weights of key tile t are formed on
+// the vector ALUs, the matrix cores already compute the scores of tile t+1
+// (issued just before, in the same basic block), so each wave keeps its own
+// MFMA pipe busy through the softmax.  K is therefore needed one tile ahead
+// of V: LDS holds a ring of STAGES K tiles (t+1 being read, t+2 in flight)
+// and a ring of 2 V tiles (t being read, t+1 in flight).
+template <int D, bool CAUSAL, int BN, int WAVES, int STAGES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                     const bf16* __restrict__ V, bf16* __restrict__ O, int B, int H_q, int H_kv,
                     int T_q, int T_kv, int n_qt, float c, int neg_q) {
+    constexpr int BM = 32 * WAVES;                // query rows per workgroup
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
     constexpr int ROWB = D * 2;                   // bytes per row
-    constexpr int TILE = kBN * ROWB;              // bytes of one K or V tile
-    constexpr int NLD = TILE / (1024 * kWaves);   // 1 KiB loads per wave per tile and operand
-    static_assert(NLD * 1024 * kWaves == TILE, "tile must split into 1 KiB wave loads");
+    constexpr int TILE = BN * ROWB;               // bytes of one K or V tile
+    constexpr int NLD = TILE / (1024 * WAVES);    // 1 KiB loads per wave per tile and operand
+    static_assert(NLD * 1024 * WAVES == TILE, "tile must split into 1 KiB wave loads");
+    static_assert(STAGES >= 3, "K ring needs t+1 in use and t+2 in flight");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * 2 * TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[(STAGES + 2) * TILE];
+    unsigned char* const kring = smem;                  // STAGES K tiles
+    unsigned char* const vring = smem + STAGES * TILE;  // 2 V tiles
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    const TileCoord tc = map_tile(blockIdx.x, B, H_q, H_kv, n_qt, CAUSAL);
+    const TileCoord tc = map_tile(blockIdx.x, B, H_q, H_kv, n_qt, BM, CAUSAL);
     const uint32_t q_bytes = (uint32_t)T_q * ROWB;
     const uint32_t kv_bytes = (uint32_t)T_kv * ROWB;
     const auto rQ = make_rsrc(Q + (size_t)(tc.b * H_q + tc.hq) * T_q * D, q_bytes);
@@ -121,41 +158,22 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const auto rO = make_rsrc(O + (size_t)(tc.b * H_q + tc.hq) * T_q * D, q_bytes);
 
     const int off = T_kv - T_q;  // bottom-right causal alignment
-    const int q0 = tc.qt * kBM;
+    const int q0 = tc.qt * BM;
     const int row0 = q0 + wave * 32;
     const int my_row = row0 + l32;
 
     // Key ranges: the workgroup's and this wave's.
-    const int last_row = min(T_q, q0 + kBM) - 1;
+    const int last_row = min(T_q, q0 + BM) - 1;
     const int kv_end = CAUSAL ? min(T_kv, last_row + off + 1) : T_kv;
-    const int n_kt = (kv_end + kBN - 1) / kBN;
+    const int n_kt = (kv_end + BN - 1) / BN;
     const int wave_last = min(T_q - 1, row0 + 31);
     const int wave_kv_end = (row0 >= T_q) ? 0 : (CAUSAL ? min(T_kv, wave_last + off + 1) : T_kv);
     const int lim = CAUSAL ? min(T_kv - 1, my_row + off) : T_kv - 1;  // last visible key of my row
 
-    // Issue the direct-to-LDS loads of key tile t (K and V) into stage t % 2.
-    // Keys past T_kv are outside the buffer range and load as zero.
-    auto issue = [&](int t) {
-        unsigned char* kst = smem + (t % kStages) * 2 * TILE;
-        unsigned char* vst = kst + TILE;
-        const int j0 = t * kBN;
-#pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const int blk = wave * NLD + n;
-            const int p = blk * 64 + lane;  // chunk slot in the tile
-            const int row = p / CPR;
-            const int logical = (p % CPR) ^ swz<CPR>(row);
-            const uint32_t boff = (uint32_t)(j0 + row) * ROWB + logical * 16;
-            buf_load_lds16(rK, kst + blk * 1024, boff);
-            buf_load_lds16(rV, vst + blk * 1024, boff);
-        }
-    };
-
-    if (n_kt > 0) issue(0);
-
     // Q fragment: B operand of S^T = K Q^T (column = query row, 8 features).
     // Rows past T_q read as zero.  A negative scale is folded into Q's sign
-    // (exact in bf16), so c > 0 below.
+    // (exact in bf16), so c > 0 below.  Issued before the tile loads so the
+    // wait for Q does not wait for them.
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
@@ -164,6 +182,29 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         qf[s] = __builtin_bit_cast(bf16x8, w);
     }
 
+    // Direct-to-LDS loads of one K or V tile.  Keys past T_kv are outside
+    // the buffer range and load as zero.
+    auto issue = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int t) {
+        const int j0 = t * BN;
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            const int blk = wave * NLD + n;
+            const int p = blk * 64 + lane;  // chunk slot in the tile
+            const int row = p / CPR;
+            const int logical = (p % CPR) ^ swz<CPR>(row);
+            buf_load_lds16(r, dst + blk * 1024, (uint32_t)(j0 + row) * ROWB + logical * 16);
+        }
+    };
+    auto issue_k = [&](int t) { issue(rK, kring + (t % STAGES) * TILE, t); };
+    auto issue_v = [&](int t) { issue(rV, vring + (t & 1) * TILE, t); };
+
+    // Prologue: K(0), V(0), K(1).  Iteration t then issues K(t+2), V(t+1).
+    if (n_kt > 0) {
+        issue_k(0);
+        issue_v(0);
+    }
+    if (n_kt > 1) issue_k(1);
+
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
@@ -171,60 +212,58 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     float l_run = 0.f;        // sum of bf16 weights relative to m_use (this lane's keys)
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-    // Lane constants of the transposing V read.
+    // Lane constants of the transposing V read and the half exchange.
+    const int xaddr = 4 * (lane ^ 32);
     const int tr_i = lane & 15;
     const int tr_key = 4 * hi + (tr_i >> 2);                  // + 16 ks + 8 r
-    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);  // + 32 db
+    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);  // feature within a 32-block
+    const int tr_c = tr_d >> 3;                                // its chunk (+ 4 db)
+    const int dbyte = (tr_d & 7) * 2;                          // byte within the chunk
+
+    STile<D, BN> s_cur, s_next;
+    if (n_kt > 0) {
+        wait_vmem_all();
+        __syncthreads();
+        if (0 < wave_kv_end) score_tile<D, BN>(s_cur, kring, qf, l32, hi);
+    }
 
     for (int t = 0; t < n_kt; ++t) {
-        wait_vmem_all();  // this wave's part of tile t has landed
-        __syncthreads();  // ... and every other wave's; tile t-1 is no longer read
-        if (t + 1 < n_kt) issue(t + 1);
-
-        const int j0 = t * kBN;
-        if (j0 >= wave_kv_end) continue;  // whole tile above this wave's diagonal
-        const unsigned char* kst = smem + (t % kStages) * 2 * TILE;
-        const unsigned char* vst = kst + TILE;
-
-        // S^T tile: rows = keys, columns = this wave's 32 query rows.
-        f32x16 sacc[kBN / 32];
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb) {
-            sacc[kb] = f32x16{};
-            const int key = kb * 32 + l32;
-            const unsigned char* krow = kst + key * ROWB;
-            const int sw = swz<CPR>(key);
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * s + hi) ^ sw) * 16));
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-            }
-        }
+        const int j0 = t * BN;
+        // K(t+1) and V(t), issued one iteration ago, must be complete in LDS
+        // (for every wave's loads), and every wave must be done reading K(t-1)
+        // and V(t-1), whose stages are refilled below.
+        wait_vmem_all();
+        __syncthreads();
+        if (t + 2 < n_kt) issue_k(t + 2);
+        if (t + 1 < n_kt) issue_v(t + 1);
+        if (j0 >= wave_kv_end) continue;  // this and all later tiles are above the diagonal
 
         // Mask (raw scores; c > 0) only where the tile needs it.
-        const bool need_mask = (j0 + kBN > T_kv) || (CAUSAL && j0 + kBN - 1 > row0 + off);
+        const bool need_mask = (j0 + BN > T_kv) || (CAUSAL && j0 + BN - 1 > row0 + off);
         if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < kBN / 32; ++kb) {
+            for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = j0 + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-                    sacc[kb][j] = key <= lim ? sacc[kb][j] : -INFINITY;
+                    s_cur.acc[kb][j] = key <= lim ? s_cur.acc[kb][j] : -INFINITY;
                 }
             }
         }
+
+        // This lane's maximum (16 keys of each block; the other half of the
+        // row lives in lane ^ 32).  The exponent base only moves when some
+        // lane's maximum exceeds it by more than 8; only then are the two
+        // halves exchanged, so both lanes of a row share one base.
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb) {
+        for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-            for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sacc[kb][j], sacc[kb][j + 1]));
+            for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(s_cur.acc[kb][j], s_cur.acc[kb][j + 1]));
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = mx * c;  // -inf when the row sees no key of this tile
-
-        // Move the exponent base only when a row's maximum grew by more than 8.
-        if (__any(m_new > m_use + 8.f)) {
-            const float m_t = fmaxf(m_use, m_new);
+        if (__any(mx * c > m_use + 8.f)) {
+            const float m_row = fmaxf(mx, swap_halves(mx, xaddr)) * c;  // -inf: no visible key yet
+            const float m_t = fmaxf(m_use, m_row);
             const float alpha = (m_t == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_t);
             l_run *= alpha;
 #pragma unroll
@@ -236,15 +275,20 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         }
         const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
 
-        // Weights, rounded to bf16 in place (the B operand of P*V), and their sum.
-        bf16x8 pb[kBN / 16];
+        // One straight-line block: the scores of tile t+1 go to the matrix
+        // cores while the weights of tile t are formed on the vector ALUs,
+        // then O += P V for tile t.  (On the last tile the next-scores
+        // read a stale stage and are discarded.)
+        score_tile<D, BN>(s_next, kring + ((t + 1) % STAGES) * TILE, qf, l32, hi);
+
+        bf16x8 pb[BN / 16];
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb) {
+        for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
             for (int j = 0; j < 16; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][j], c, -m_sub));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][j + 1], c, -m_sub));
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[kb][j], c, -m_sub));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[kb][j + 1], c, -m_sub));
                 const bf16x2 pp = {(bf16)p0, (bf16)p1};
                 if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
                 else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
@@ -257,26 +301,30 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         // O^T += V^T P^T.  Lane (feature d, half hi) needs V for keys
         // 16ks + 4hi + {0..3} and 16ks + 8 + 4hi + {0..3}, the keys its P
         // operand holds; two transposing reads deliver exactly those.
+        const unsigned char* vst = vring + (t & 1) * TILE;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const int d = db * 32 + tr_d;
-            const int dchunk = d >> 3;
-            const int dbyte = (d & 7) * 2;
+        for (int ks = 0; ks < BN / 16; ++ks) {
+            const int k_lo = ks * 16 + tr_key;
+            const int k_hi = k_lo + 8;
+            const unsigned char* vlo = vst + k_lo * ROWB + dbyte;
+            const unsigned char* vhi = vst + k_hi * ROWB + dbyte;
+            const int sw_lo = swz<CPR>(k_lo), sw_hi = swz<CPR>(k_hi);
 #pragma unroll
-            for (int ks = 0; ks < kBN / 16; ++ks) {
-                const int k_lo = ks * 16 + tr_key;
-                const int k_hi = k_lo + 8;
-                const bf16x4 lo = lds_read_tr16(vst + k_lo * ROWB + ((dchunk ^ swz<CPR>(k_lo)) * 16) + dbyte);
-                const bf16x4 h4 = lds_read_tr16(vst + k_hi * ROWB + ((dchunk ^ swz<CPR>(k_hi)) * 16) + dbyte);
+            for (int db = 0; db < D / 32; ++db) {
+                const int dchunk = db * 4 + tr_c;
+                const bf16x4 lo = lds_read_tr16(vlo + ((dchunk ^ sw_lo) * 16));
+                const bf16x4 h4 = lds_read_tr16(vhi + ((dchunk ^ sw_hi) * 16));
                 const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
             }
         }
+        SCHED_HINTS
+        s_cur = s_next;
     }
 
     // Epilogue: O = O_acc / l, rounded once to bf16.  Rows past T_q fall
     // outside the buffer range and their stores are dropped.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = l_run + swap_halves(l_run, xaddr);
     const float inv = 1.f / l_tot;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -291,14 +339,21 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
 }
 
+template <int D, bool CAUSAL, int BN, int WAVES, int STAGES>
+hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
+    constexpr int BM = 32 * WAVES;
+    const int n_qt = (a.T_q + BM - 1) / BM;
+    const long long grid = (long long)a.B * a.H_q * n_qt;
+    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, BN, WAVES, STAGES>, dim3((unsigned)grid),
+                         dim3(64 * WAVES), 0, s, static_cast<const bf16*>(a.q),
+                         static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                         static_cast<bf16*>(a.o), a.B, a.H_q, a.H_kv, a.T_q, a.T_kv, n_qt, a.c_log2,
+                         a.neg_q);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
-    const int n_qt = (a.T_q + kBM - 1) / kBM;
-    const long long grid = (long long)a.B * a.H_q * n_qt;
-    return launch_kernel(prefill_bf16_kernel<D, CAUSAL>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                         static_cast<const bf16*>(a.v), static_cast<bf16*>(a.o), a.B, a.H_q, a.H_kv,
-                         a.T_q, a.T_kv, n_qt, a.c_log2, a.neg_q);
+    return launch_cfg<D, CAUSAL, PF_BN, PF_WAVES, PF_STAGES>(a, s);
 }
 
 }  // namespace
