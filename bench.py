@@ -93,7 +93,97 @@ def cpu_baseline(budget_s=15.0):
     }
 
 
+KERNELS = {
+    # name in profiles/ : (kernel-name substring, source files, algorithmic bytes per launch)
+    "prefill_bf16_T8192_D128_gqa": ("prefill_bf16_kernel", ["prefill_bf16.hip", "kernel_common.h"]),
+    "decode_bf16_B64_T4096_D128": ("decode_split_kernel", ["decode_bf16.hip", "kernel_common.h"]),
+}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
+    """Turn rocprofv3 CSV output (a --kernel-trace --stats run and two --pmc
+    runs, FETCH_SIZE then WRITE_SIZE, each with a device copy of copy_mib MiB
+    for calibration) into the summaries kept under profiles/."""
+    import glob
+    from transformer_scaled_dot_flash_amd.workloads import DECODE_HEADLINE as wd
+    from transformer_scaled_dot_flash_amd.workloads import PREFILL_HEADLINE as wp
+    stats = _csv_rows(glob.glob(f"{trace_dir}/**/*kernel_stats.csv", recursive=True)[0])
+
+    def counter(d, name):
+        out = {}
+        for r in _csv_rows(glob.glob(f"{d}/**/*counter_collection.csv", recursive=True)[0]):
+            if r["Counter_Name"] == name:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    fetch = counter(fetch_dir, "FETCH_SIZE")
+    write = counter(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib << 20
+
+    def pick(d, sub):
+        ks = [k for k in d if sub in k]
+        return d[ks[0]] if ks else None
+
+    f_copy = pick(fetch, "copyBuffer")
+    w_copy = pick(write, "copyBuffer")
+    f_scale = copy_bytes / (f_copy * 1024.0)
+    w_scale = copy_bytes / (w_copy * 1024.0)
+    csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
+    algo = {"prefill_bf16_T8192_D128_gqa": wp.bytes(), "decode_bf16_B64_T4096_D128": wd.bytes()}
+    for name, (sub, files) in KERNELS.items():
+        st = [r for r in stats if sub in r["Name"]]
+        if not st:
+            continue
+        st = st[0]
+        fk, wk = pick(fetch, sub), pick(write, sub)
+        fetch_b = fk * 1024.0 * f_scale
+        write_b = wk * 1024.0 * w_scale
+        digest = source_digest([csrc / f for f in files])
+        rec = {
+            "kernel": st["Name"],
+            "source_sha256": digest,
+            "calls": int(st["Calls"]),
+            "avg_duration_us": round(float(st["AverageNs"]) / 1e3, 2),
+            "min_duration_us": round(float(st["MinNs"]) / 1e3, 2),
+            "fetch_size_kib_raw": fk,
+            "write_size_kib_raw": wk,
+            "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib_raw": f_copy,
+                                 "write_kib_raw": w_copy, "fetch_scale": round(f_scale, 4),
+                                 "write_scale": round(w_scale, 4)},
+            "hbm_fetch_bytes_per_launch": round(fetch_b),
+            "hbm_write_bytes_per_launch": round(write_b),
+            "hbm_bytes_per_launch": round(fetch_b + write_b),
+            "algorithmic_bytes_per_launch": algo[name],
+        }
+        (PROFILES / f"{name}_traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
+        md = [f"# {name}", "", f"Kernel: `{st['Name']}`", "",
+              "Commands (from the repository root on the GPU host):", "", "```", command_note, "```", "",
+              "| figure | value |", "|---|---|",
+              f"| dispatches | {rec['calls']} |",
+              f"| average duration (kernel trace) | {rec['avg_duration_us']} us |",
+              f"| minimum duration | {rec['min_duration_us']} us |",
+              f"| FETCH_SIZE raw / dispatch | {fk:.0f} KiB |",
+              f"| WRITE_SIZE raw / dispatch | {wk:.0f} KiB |",
+              f"| copy calibration ({copy_mib} MiB read + written) | FETCH x{f_scale:.3f}, WRITE x{w_scale:.3f} |",
+              f"| HBM bytes fetched / launch (scaled) | {fetch_b / 2**20:.1f} MiB |",
+              f"| HBM bytes written / launch (scaled) | {write_b / 2**20:.1f} MiB |",
+              f"| algorithmic bytes / launch | {algo[name] / 2**20:.1f} MiB |",
+              f"| source sha256 (kernel + common header) | `{digest[:16]}...` |", ""]
+        (PROFILES / f"{name}.md").write_text("\n".join(md))
+        print(f"wrote profiles/{name}.md")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        # python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR COPY_MIB "commands"
+        summarize(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
