@@ -2,68 +2,64 @@
 //
 // Method: FlashAttention-style tiling with online softmax (AIInfraGuide
 // "3.3 Self-Attention机制深入理解", sections 7.3, 12.2, 12.3): each
-// workgroup owns 128 query rows of one (batch, q head), walks the key/value
-// tiles of its kv head, keeps a running row maximum m, a running exponential
-// sum l and an unnormalised output accumulator in registers, rescales them
-// when m grows, and divides by l once at the end.  Scores and weights never
-// leave the chip.
+// workgroup owns a block of query rows of one (batch, q head), walks the
+// key/value tiles of its kv head, keeps a running row maximum m, a running
+// exponential sum l and an unnormalised output accumulator in registers,
+// rescales them when m grows, and divides by l once at the end.  Scores and
+// weights never leave the chip.
 //
 // gfx950 mapping:
-//   * 4 waves x 32 query rows, two workgroups per CU (<= 256 registers per
-//     lane), so one wave's softmax overlaps the other's matrix work.
-//   * Each wave computes S^T = K * Q^T for 32 keys at a time with
-//     v_mfma_f32_32x32x16_bf16: one query row per lane column and 16 keys per
-//     lane, so the row maximum is in-lane plus one exchange with lane^32.
-//   * The same layout is the B operand of O^T = V^T * P^T: weights are
-//     rounded to bf16 in place and never move between lanes.  The V^T A
-//     operand comes straight from the row-major V tile with the transposing
-//     LDS read ds_read_b64_tr_b16.
+//   * Each wave owns RB blocks of 32 query rows.  It computes S^T = K * Q^T
+//     for 32 keys at a time with v_mfma_f32_32x32x16_bf16: one query row per
+//     lane column and 16 keys per lane, so the row maximum is in-lane plus
+//     one exchange with lane^32.  Every K fragment read from LDS feeds RB
+//     MFMAs, and so does every V fragment: LDS read traffic per FLOP falls
+//     as 1/RB.  (LDS delivers about 128 B/clock per CU, exactly what one
+//     32x32x16 MFMA per SIMD per 32 clocks consumes at RB = 1.)
+//   * The score accumulator layout is the B operand of O^T = V^T * P^T:
+//     weights are rounded to bf16 in place and never move between lanes.
+//     The V^T A operand comes straight from the row-major V tile with the
+//     transposing LDS read ds_read_b64_tr_b16.
 //   * K and V tiles go from HBM to LDS with 16-byte buffer loads that write
-//     LDS directly (no register staging), double-buffered: the next tile is
-//     in flight while the current one is consumed.  Each 1 KiB load covers
-//     whole rows; an XOR swizzle of the 16-byte chunks (chosen through the
-//     per-lane source address) keeps both the K reads and the transposing V
-//     reads free of bank conflicts.
+//     LDS directly (no register staging).  Each 1 KiB load covers whole rows;
+//     an XOR swizzle of the 16-byte chunks (chosen through the per-lane
+//     source address) keeps the K reads and the transposing V reads free of
+//     bank conflicts on the 64-bank LDS.
+//   * Per wave, the scores of key tile t+1 are issued on the matrix cores in
+//     the same basic block that forms tile t's weights on the vector ALUs.
+//     K therefore runs one tile ahead of V: LDS holds a ring of KST K tiles
+//     and a ring of 2 V tiles.
 //   * Softmax in the exp2 domain: the row maximum is taken on raw scores,
-//     one FMA forms score * scale * log2(e) - max, and the maximum used for
-//     the exponent is only moved when a row's maximum grows by more than 8
-//     (so weights stay <= 2^8 and the O rescale is rare; the final O / l is
-//     the same for any base).  Row sums add the bf16-rounded weights with
-//     v_dot2_f32_bf16, so O stays a convex combination of V's rows.
+//     one FMA forms score * scale * log2(e) - base, and the base is only
+//     moved when a row's maximum grows by more than 8 (so weights stay
+//     <= 2^8 and the O rescale is rare; the final O / l is the same for any
+//     base).  Row sums add the bf16-rounded weights with v_dot2_f32_bf16, so
+//     O stays a convex combination of V's rows.
 //   * Causal: key tiles wholly above the diagonal are never visited (per
-//     workgroup) or skipped (per wave); only tiles that cross the diagonal or
-//     the end of the keys pay for the element mask (Ch. 11 "Attention" page,
-//     section 11.8.3), using exact tile bounds.
+//     workgroup) or skipped (per wave and row block); only tiles that cross
+//     the diagonal or the end of the keys pay for the element mask (Ch. 11
+//     "Attention" page, section 11.8.3), using exact tile bounds.
 //   * Workgroups run heaviest query tile first (causal work grows along the
 //     sequence) and, when the kv-head count allows, all workgroups of one kv
 //     head run on one XCD so its K/V stay in that XCD's L2.
+//
+// Configurations (RB = 1, two waves per SIMD): 8 waves x 32 rows per
+// workgroup for large problems (one K/V tile in LDS serves 256 query rows,
+// one workgroup per CU), 4 waves x 32 rows for small ones (twice as many
+// workgroups, two per CU).  RB = 2 halves the LDS read traffic per
+// FLOP but needs ~480 registers per lane, i.e. one wave per SIMD, and was
+// measured slower (the accumulators spill between AGPRs and VGPRs).
 #include "kernel_common.h"
 
 namespace attn {
 namespace {
-
-#ifndef SCHED_HINTS
-#define SCHED_HINTS
-#endif
-
-// Tile configuration: keys per tile, waves (x 32 query rows) per workgroup,
-// depth of the LDS tile ring.
-#ifndef PF_BN
-#define PF_BN 64
-#endif
-#ifndef PF_WAVES
-#define PF_WAVES 4
-#endif
-#ifndef PF_STAGES
-#define PF_STAGES 3
-#endif
 
 struct TileCoord {
     int qt, b, hq, hk;
 };
 
 // Workgroup id -> (query tile, batch, q head, kv head).
-__device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt, int BM, bool causal) {
+__device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt, bool causal) {
     const int G = H_q / H_kv;
     const int units = B * H_kv;  // (batch, kv head) pairs
     int qt_rev, unit, g;
@@ -94,20 +90,24 @@ __device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt,
     return t;
 }
 
-// One key tile of S^T = K Q^T for this wave: kBN/32 independent MFMA chains
-// over the D/16 feature steps, interleaved.
-template <int D, int BN>
+// Scores of one key tile for all RB row blocks of this wave.
+template <int BN, int RB>
 struct STile {
-    f32x16 acc[BN / 32];
+    f32x16 acc[RB][BN / 32];
 };
 
-template <int D, int BN>
-__device__ inline void score_tile(STile<D, BN>& st, const unsigned char* kst, const bf16x8* qf,
-                                  int l32, int hi) {
+// S^T = K Q^T for one tile: RB * BN/32 independent MFMA chains over the D/16
+// feature steps; each K fragment (one ds_read_b128) feeds RB MFMAs.
+template <int D, int BN, int RB>
+__device__ inline void score_tile(STile<BN, RB>& st, const unsigned char* kst,
+                                  const bf16x8 (&qf)[RB][D / 16], int l32, int hi) {
     constexpr int CPR = D / 8;
     constexpr int ROWB = D * 2;
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) st.acc[kb] = f32x16{};
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) st.acc[rb][kb] = f32x16{};
+    }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
@@ -115,33 +115,30 @@ __device__ inline void score_tile(STile<D, BN>& st, const unsigned char* kst, co
             const int key = kb * 32 + l32;
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(
                 kst + key * ROWB + (((2 * s + hi) ^ swz<CPR>(key)) * 16));
-            st.acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st.acc[kb], 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                st.acc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][s], st.acc[rb][kb], 0, 0, 0);
         }
     }
 }
 
-// Software pipeline per wave: while the weights of key tile t are formed on
-// the vector ALUs, the matrix cores already compute the scores of tile t+1
-// (issued just before, in the same basic block), so each wave keeps its own
-// MFMA pipe busy through the softmax.  K is therefore needed one tile ahead
-// of V: LDS holds a ring of STAGES K tiles (t+1 being read, t+2 in flight)
-// and a ring of 2 V tiles (t being read, t+1 in flight).
-template <int D, bool CAUSAL, int BN, int WAVES, int STAGES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+template <int D, bool CAUSAL, int RB, int BN, int WAVES, int KST, int WPE>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
 prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                     const bf16* __restrict__ V, bf16* __restrict__ O, int B, int H_q, int H_kv,
                     int T_q, int T_kv, int n_qt, float c, int neg_q) {
-    constexpr int BM = 32 * WAVES;                // query rows per workgroup
+    constexpr int WROWS = 32 * RB;                // query rows per wave
+    constexpr int BM = WROWS * WAVES;             // query rows per workgroup
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
     constexpr int ROWB = D * 2;                   // bytes per row
     constexpr int TILE = BN * ROWB;               // bytes of one K or V tile
-    constexpr int NLD = TILE / (1024 * WAVES);    // 1 KiB loads per wave per tile and operand
+    constexpr int NLD = TILE / (1024 * WAVES);    // 1 KiB loads per wave per tile
     static_assert(NLD * 1024 * WAVES == TILE, "tile must split into 1 KiB wave loads");
-    static_assert(STAGES >= 3, "K ring needs t+1 in use and t+2 in flight");
+    static_assert(KST >= 3, "K ring needs t+1 in use and t+2 in flight");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[(STAGES + 2) * TILE];
-    unsigned char* const kring = smem;                  // STAGES K tiles
-    unsigned char* const vring = smem + STAGES * TILE;  // 2 V tiles
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[(KST + 2) * TILE];
+    unsigned char* const kring = smem;               // KST K tiles
+    unsigned char* const vring = smem + KST * TILE;  // 2 V tiles
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -149,7 +146,7 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    const TileCoord tc = map_tile(blockIdx.x, B, H_q, H_kv, n_qt, BM, CAUSAL);
+    const TileCoord tc = map_tile(blockIdx.x, B, H_q, H_kv, n_qt, CAUSAL);
     const uint32_t q_bytes = (uint32_t)T_q * ROWB;
     const uint32_t kv_bytes = (uint32_t)T_kv * ROWB;
     const auto rQ = make_rsrc(Q + (size_t)(tc.b * H_q + tc.hq) * T_q * D, q_bytes);
@@ -159,27 +156,33 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
     const int off = T_kv - T_q;  // bottom-right causal alignment
     const int q0 = tc.qt * BM;
-    const int row0 = q0 + wave * 32;
-    const int my_row = row0 + l32;
+    const int row0 = q0 + wave * WROWS;  // first row of this wave
 
-    // Key ranges: the workgroup's and this wave's.
+    // Key ranges: the workgroup's, this wave's, each row block's.
     const int last_row = min(T_q, q0 + BM) - 1;
     const int kv_end = CAUSAL ? min(T_kv, last_row + off + 1) : T_kv;
     const int n_kt = (kv_end + BN - 1) / BN;
-    const int wave_last = min(T_q - 1, row0 + 31);
-    const int wave_kv_end = (row0 >= T_q) ? 0 : (CAUSAL ? min(T_kv, wave_last + off + 1) : T_kv);
-    const int lim = CAUSAL ? min(T_kv - 1, my_row + off) : T_kv - 1;  // last visible key of my row
-
-    // Q fragment: B operand of S^T = K Q^T (column = query row, 8 features).
-    // Rows past T_q read as zero.  A negative scale is folded into Q's sign
-    // (exact in bf16), so c > 0 below.  Issued before the tile loads so the
-    // wait for Q does not wait for them.
-    bf16x8 qf[D / 16];
+    int rb_kv_end[RB];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        u32x4 w = buf_load_b128(rQ, (uint32_t)(my_row * D + 16 * s + 8 * hi) * 2);
-        if (neg_q) w ^= 0x80008000u;
-        qf[s] = __builtin_bit_cast(bf16x8, w);
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r0 = row0 + rb * 32;
+        const int rlast = min(T_q - 1, r0 + 31);
+        rb_kv_end[rb] = (r0 >= T_q) ? 0 : (CAUSAL ? min(T_kv, rlast + off + 1) : T_kv);
+    }
+    const int wave_kv_end = rb_kv_end[RB - 1];  // the last row block sees the most keys
+
+    // Q fragments: B operands of S^T = K Q^T (column = query row, 8 features).
+    // Rows past T_q read as zero.  A negative scale is folded into Q's sign
+    // (exact in bf16), so c > 0 below.  Issued before the tile loads.
+    bf16x8 qf[RB][D / 16];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            u32x4 w = buf_load_b128(rQ, (uint32_t)((row0 + rb * 32 + l32) * D + 16 * s + 8 * hi) * 2);
+            if (neg_q) w ^= 0x80008000u;
+            qf[rb][s] = __builtin_bit_cast(bf16x8, w);
+        }
     }
 
     // Direct-to-LDS loads of one K or V tile.  Keys past T_kv are outside
@@ -195,7 +198,7 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             buf_load_lds16(r, dst + blk * 1024, (uint32_t)(j0 + row) * ROWB + logical * 16);
         }
     };
-    auto issue_k = [&](int t) { issue(rK, kring + (t % STAGES) * TILE, t); };
+    auto issue_k = [&](int t) { issue(rK, kring + (t % KST) * TILE, t); };
     auto issue_v = [&](int t) { issue(rV, vring + (t & 1) * TILE, t); };
 
     // Prologue: K(0), V(0), K(1).  Iteration t then issues K(t+2), V(t+1).
@@ -205,11 +208,16 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
     if (n_kt > 1) issue_k(1);
 
-    f32x16 oacc[D / 32];
+    f32x16 oacc[RB][D / 32];
+    float m_use[RB];  // base of the exponent (log2 units), per row
+    float l_run[RB];  // sum of bf16 weights relative to m_use (this lane's keys)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_use = -INFINITY;  // base of the exponent (log2 units), per row
-    float l_run = 0.f;        // sum of bf16 weights relative to m_use (this lane's keys)
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[rb][db] = f32x16{};
+        m_use[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+    }
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
     // Lane constants of the transposing V read and the half exchange.
@@ -220,11 +228,11 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int tr_c = tr_d >> 3;                                // its chunk (+ 4 db)
     const int dbyte = (tr_d & 7) * 2;                          // byte within the chunk
 
-    STile<D, BN> s_cur, s_next;
+    STile<BN, RB> s_cur, s_next;
     if (n_kt > 0) {
         wait_vmem_all();
         __syncthreads();
-        if (0 < wave_kv_end) score_tile<D, BN>(s_cur, kring, qf, l32, hi);
+        if (0 < wave_kv_end) score_tile<D, BN, RB>(s_cur, kring, qf, l32, hi);
     }
 
     for (int t = 0; t < n_kt; ++t) {
@@ -238,69 +246,85 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         if (t + 1 < n_kt) issue_v(t + 1);
         if (j0 >= wave_kv_end) continue;  // this and all later tiles are above the diagonal
 
-        // Mask (raw scores; c > 0) only where the tile needs it.
-        const bool need_mask = (j0 + BN > T_kv) || (CAUSAL && j0 + BN - 1 > row0 + off);
-        if (need_mask) {
+        // Per row block: mask, base update.
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            if (j0 >= rb_kv_end[rb]) continue;  // this block's rows see none of these keys
+            const int r0 = row0 + rb * 32;
+            const bool need_mask = (j0 + BN > T_kv) || (CAUSAL && j0 + BN - 1 > r0 + off);
+            if (need_mask) {
+                const int lim = CAUSAL ? min(T_kv - 1, r0 + l32 + off) : T_kv - 1;
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = j0 + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+                        s_cur.acc[rb][kb][j] = key <= lim ? s_cur.acc[rb][kb][j] : -INFINITY;
+                    }
+                }
+            }
+
+            // This lane's maximum (16 keys of each block; the other half of
+            // the row lives in lane ^ 32).  The base only moves when some
+            // lane's maximum exceeds it by more than 8; only then are the two
+            // halves exchanged, so both lanes of a row share one base.
+            float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = j0 + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-                    s_cur.acc[kb][j] = key <= lim ? s_cur.acc[kb][j] : -INFINITY;
+                for (int j = 0; j < 16; j += 2)
+                    mx = fmaxf(mx, fmaxf(s_cur.acc[rb][kb][j], s_cur.acc[rb][kb][j + 1]));
+            }
+            if (__any(mx * c > m_use[rb] + 8.f)) {
+                const float m_row = fmaxf(mx, swap_halves(mx, xaddr)) * c;  // -inf: no visible key yet
+                const float m_t = fmaxf(m_use[rb], m_row);
+                const float alpha = (m_t == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_use[rb] - m_t);
+                l_run[rb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) oacc[rb][db][j] *= alpha;
                 }
+                m_use[rb] = m_t;
             }
         }
-
-        // This lane's maximum (16 keys of each block; the other half of the
-        // row lives in lane ^ 32).  The exponent base only moves when some
-        // lane's maximum exceeds it by more than 8; only then are the two
-        // halves exchanged, so both lanes of a row share one base.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-            for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(s_cur.acc[kb][j], s_cur.acc[kb][j + 1]));
-        }
-        if (__any(mx * c > m_use + 8.f)) {
-            const float m_row = fmaxf(mx, swap_halves(mx, xaddr)) * c;  // -inf: no visible key yet
-            const float m_t = fmaxf(m_use, m_row);
-            const float alpha = (m_t == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_t);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-            }
-            m_use = m_t;
-        }
-        const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
 
         // One straight-line block: the scores of tile t+1 go to the matrix
         // cores while the weights of tile t are formed on the vector ALUs,
-        // then O += P V for tile t.  (On the last tile the next-scores
-        // read a stale stage and are discarded.)
-        score_tile<D, BN>(s_next, kring + ((t + 1) % STAGES) * TILE, qf, l32, hi);
+        // then O += P V for tile t.  (After the wave's last tile the
+        // next-scores read a stale stage and are discarded.)
+        score_tile<D, BN, RB>(s_next, kring + ((t + 1) % KST) * TILE, qf, l32, hi);
 
-        bf16x8 pb[BN / 16];
-        float ps0 = 0.f, ps1 = 0.f;
+        bf16x8 pb[RB][BN / 16];
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
+        for (int rb = 0; rb < RB; ++rb) {
+            // A row block with no visible key in this tile contributes
+            // nothing: its weights are zero.
+            const bool live = j0 < rb_kv_end[rb];
+            const float m_sub = (m_use[rb] == -INFINITY) ? 0.f : m_use[rb];
+            const float cc = live ? c : 0.f;
+            const float msub = live ? m_sub : INFINITY;
+            float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[kb][j], c, -m_sub));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[kb][j + 1], c, -m_sub));
-                const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
-                else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
-                pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
-                pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
+            for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+                for (int j = 0; j < 16; j += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[rb][kb][j], cc, -msub));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[rb][kb][j + 1], cc, -msub));
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
+                    else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
+                    pb[rb][kb * 2 + (j >> 3)][j & 7] = pp[0];
+                    pb[rb][kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
+                }
             }
+            l_run[rb] += ps0 + ps1;
         }
-        l_run += ps0 + ps1;
 
         // O^T += V^T P^T.  Lane (feature d, half hi) needs V for keys
         // 16ks + 4hi + {0..3} and 16ks + 8 + 4hi + {0..3}, the keys its P
-        // operand holds; two transposing reads deliver exactly those.
+        // operand holds; two transposing reads deliver exactly those, and
+        // each V fragment feeds RB MFMAs.
         const unsigned char* vst = vring + (t & 1) * TILE;
 #pragma unroll
         for (int ks = 0; ks < BN / 16; ++ks) {
@@ -315,45 +339,60 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                 const bf16x4 lo = lds_read_tr16(vlo + ((dchunk ^ sw_lo) * 16));
                 const bf16x4 h4 = lds_read_tr16(vhi + ((dchunk ^ sw_hi) * 16));
                 const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][ks], oacc[rb][db], 0, 0, 0);
             }
         }
-        SCHED_HINTS
         s_cur = s_next;
     }
 
     // Epilogue: O = O_acc / l, rounded once to bf16.  Rows past T_q fall
     // outside the buffer range and their stores are dropped.
-    const float l_tot = l_run + swap_halves(l_run, xaddr);
-    const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l_tot = l_run[rb] + swap_halves(l_run[rb], xaddr);
+        const float inv = 1.f / l_tot;
+        const int my_row = row0 + rb * 32 + l32;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            bf16x4 w;
+        for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w[r] = (bf16)(oacc[db][4 * g4 + r] * inv);
-            buf_store_b64(__builtin_bit_cast(u32x2, w), rO,
-                          (uint32_t)(my_row * D + db * 32 + 8 * g4 + 4 * hi) * 2);
+            for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 w;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[r] = (bf16)(oacc[rb][db][4 * g4 + r] * inv);
+                buf_store_b64(__builtin_bit_cast(u32x2, w), rO,
+                              (uint32_t)(my_row * D + db * 32 + 8 * g4 + 4 * hi) * 2);
+            }
         }
     }
 }
 
-template <int D, bool CAUSAL, int BN, int WAVES, int STAGES>
+template <int D, bool CAUSAL, int RB, int BN, int WAVES, int KST, int WPE>
 hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
-    constexpr int BM = 32 * WAVES;
+    constexpr int BM = 32 * RB * WAVES;
     const int n_qt = (a.T_q + BM - 1) / BM;
     const long long grid = (long long)a.B * a.H_q * n_qt;
-    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, BN, WAVES, STAGES>, dim3((unsigned)grid),
+    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, RB, BN, WAVES, KST, WPE>, dim3((unsigned)grid),
                          dim3(64 * WAVES), 0, s, static_cast<const bf16*>(a.q),
                          static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                          static_cast<bf16*>(a.o), a.B, a.H_q, a.H_kv, a.T_q, a.T_kv, n_qt, a.c_log2,
                          a.neg_q);
 }
 
+#ifndef PF_FORCE
+#define PF_FORCE 0
+#endif
+
+// Large problems (at least two 256-row workgroups per CU): 8 waves, one
+// workgroup per CU.  Otherwise 4 waves, two workgroups per CU.  Both use
+// 80 KiB of LDS (K ring of 3, V ring of 2).
 template <int D, bool CAUSAL>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
-    return launch_cfg<D, CAUSAL, PF_BN, PF_WAVES, PF_STAGES>(a, s);
+    const long long wg_big = (long long)a.B * a.H_q * ((a.T_q + 255) / 256);
+    const bool big = PF_FORCE == 2 || (PF_FORCE == 0 && wg_big >= 512);
+    if (big) return launch_cfg<D, CAUSAL, 1, 64, 8, 3, 2>(a, s);
+    return launch_cfg<D, CAUSAL, 1, 64, 4, 3, 2>(a, s);
 }
 
 }  // namespace
