@@ -20,7 +20,8 @@
 // The split pass uses the prefill kernel's MFMA layout with the query heads
 // of the group as the 32 MFMA columns: S^T = K Q^T on
 // v_mfma_f32_32x32x16_bf16, then O^T += V^T P^T with the V^T operand read by
-// ds_read_b64_tr_b16.  Each wave streams 32-key tiles of K and V from HBM
+// ds_read_b64_tr_b16 (issued as inline assembly, see ds_read_tr16_asm).
+// Each wave streams 32-key tiles of K and V from HBM
 // straight into its own LDS ring of kStages tiles with 16-byte buffer loads
 // (each 1 KiB load covers four whole rows), keeping kStages - 1 tiles in
 // flight while it consumes one; waves never synchronise with each other.
@@ -116,17 +117,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         qf[s] = __builtin_bit_cast(bf16x8, w);
     }
 
-    f32x16 oacc[D / 32];
+    f32x16 oacc[1][D / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    for (int db = 0; db < D / 32; ++db) oacc[0][db] = f32x16{};
     float m_use = -INFINITY;
     float l_run = 0.f;
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
     const int xaddr = 4 * (lane ^ 32);
-    const int tr_i = lane & 15;
-    const int tr_key = 4 * hi + (tr_i >> 2);
-    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
+    uint32_t voff[2][D / 32];  // V^T read offsets within a tile
+    pv_lane_offsets<D>(voff, lane);
 
     for (int t = 0; t < n_t; ++t) {
         // The Q loads were issued after the first tiles, so they are covered
@@ -168,13 +168,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+                for (int j = 0; j < 16; ++j) oacc[0][db][j] *= alpha;
             }
             m_use = m_t;
         }
         const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
 
-        bf16x8 pb[2];
+        bf16x8 pb[1][2];
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
@@ -183,26 +183,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
             const bf16x2 pp = {(bf16)p0, (bf16)p1};
             if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
             else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
-            pb[j >> 3][j & 7] = pp[0];
-            pb[j >> 3][(j & 7) + 1] = pp[1];
+            pb[0][j >> 3][j & 7] = pp[0];
+            pb[0][j >> 3][(j & 7) + 1] = pp[1];
         }
         l_run += ps0 + ps1;
 
+        // O^T += V^T P^T over the tile's two key steps.  All of this wave's
+        // tile loads are drained first: with ~500 waves each streaming its
+        // own key range, keeping about one tile per wave in flight reads HBM
+        // faster (measured 6.1 vs 5.7 TB/s) than letting two stay in flight.
+        wait_vmem_all();
+        const uint32_t vbase = lds_u32(vst);
+        uint32_t va[2][D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const int d = db * 32 + tr_d;
-            const int dchunk = d >> 3;
-            const int dbyte = (d & 7) * 2;
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int k_lo = ks * 16 + tr_key;
-                const int k_hi = k_lo + 8;
-                const bf16x4 lo = lds_read_tr16(vst + k_lo * ROWB + ((dchunk ^ swz<CPR>(k_lo)) * 16) + dbyte);
-                const bf16x4 h4 = lds_read_tr16(vst + k_hi * ROWB + ((dchunk ^ swz<CPR>(k_hi)) * 16) + dbyte);
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[db], 0, 0, 0);
-            }
+            for (int db = 0; db < D / 32; ++db) va[h][db] = vbase + voff[h][db];
         }
+        pv_tile<D, kBN / 16, 1>(oacc, pb, va);
     }
 
     const float l_tot = l_run + swap_halves(l_run, xaddr);
@@ -218,7 +216,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
             for (int g4 = 0; g4 < 4; ++g4) {
                 bf16x4 w;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) w[r] = (bf16)(oacc[db][4 * g4 + r] * inv);
+                for (int r = 0; r < 4; ++r) w[r] = (bf16)(oacc[0][db][4 * g4 + r] * inv);
                 *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g4) = w;
             }
         }
@@ -230,8 +228,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 w = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
-                             oacc[db][4 * g4 + 3]};
+            const f32x4 w = {oacc[0][db][4 * g4], oacc[0][db][4 * g4 + 1], oacc[0][db][4 * g4 + 2],
+                             oacc[0][db][4 * g4 + 3]};
             *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g4) = w;
         }
     }

@@ -39,11 +39,92 @@ __device__ inline u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t byte_of
 __device__ inline void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_block, uint32_t byte_off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 16, (int)byte_off, 0, 0, 0);
 }
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// source lane r points at 4 consecutive bf16 values R[r][0..3]; destination
-// lane i receives R[i/4 + 4k][i%4] for k = 0..3.
-__device__ inline bf16x4 lds_read_tr16(const void* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+// Byte address of an LDS object (the 32-bit offset LDS instructions take).
+__device__ inline uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16) of lds_addr + OFF.  Within each
+// group of 16 lanes, source lane r points at 4 consecutive bf16 values
+// R[r][0..3]; destination lane i receives R[i/4 + 4k][i%4] for k = 0..3.
+//
+// Issued as inline assembly on purpose: for the compiler's own intrinsic the
+// compiler cannot tell the read apart from the LDS written by outstanding
+// buffer-to-LDS loads and puts a full vmcnt(0) wait in front of it, which
+// stalls every wave until all of its tile prefetches have landed.  The
+// compiler does not track this read, so its result may only be used after
+// lds_wait_bind; the "memory" clobber keeps it in program order with every
+// other memory access.
+template <int OFF>
+__device__ inline bf16x4 ds_read_tr16_asm(uint32_t lds_addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
+    bf16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "n"(OFF) : "memory");
+    return r;
+}
+
+// s_waitcnt lgkmcnt(N) that also redefines the fragments f, so no use of f
+// can be scheduled before it.  LDS operations complete in issue order, so
+// once at most N are outstanding, every read issued before the last N has
+// completed (other LDS or scalar operations only make the wait stricter).
+template <int N, int ND>
+__device__ inline void lds_wait_bind(bf16x4 (&f)[2][ND]) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+    static_assert(ND == 2 || ND == 4, "two or four 32-feature blocks");
+    if constexpr (ND == 4)
+        asm volatile("s_waitcnt lgkmcnt(%8)"
+                     : "+v"(f[0][0]), "+v"(f[0][1]), "+v"(f[0][2]), "+v"(f[0][3]), "+v"(f[1][0]),
+                       "+v"(f[1][1]), "+v"(f[1][2]), "+v"(f[1][3])
+                     : "n"(N));
+    else
+        asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(f[0][0]), "+v"(f[0][1]), "+v"(f[1][0]), "+v"(f[1][1]) : "n"(N));
+}
+
+// O^T += V^T P^T over one V tile in LDS (row-major, swizzled by swz), for
+// RB blocks of 32 query columns.  Lane (feature d, half hi) needs V for the
+// keys 16ks + 4hi + {0..3} and 16ks + 8 + 4hi + {0..3} that its P operand
+// (the score accumulator layout) holds; two transposing reads per 32-feature
+// block deliver exactly those.  va[h][db] is the lane's address of key step 0
+// for the low (h = 0) and high (h = 1) key group of feature block db; key step
+// ks adds 16 rows.  The reads of step ks + 1 are in flight while the MFMAs
+// of step ks run; each V fragment feeds RB MFMAs.
+template <int KS, int D>
+__device__ inline void pv_issue(bf16x4 (&f)[2][D / 32], const uint32_t (&va)[2][D / 32]) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        f[0][db] = ds_read_tr16_asm<KS * 16 * D * 2>(va[0][db]);
+        f[1][db] = ds_read_tr16_asm<KS * 16 * D * 2>(va[1][db]);
+    }
+}
+template <int KS, int D, int NKS, int RB>
+__device__ inline void pv_step(f32x16 (&oacc)[RB][D / 32], const bf16x8 (&pb)[RB][NKS],
+                               bf16x4 (&cur)[2][D / 32], bf16x4 (&nxt)[2][D / 32],
+                               const uint32_t (&va)[2][D / 32]) {
+    constexpr bool more = KS + 1 < NKS;
+    if constexpr (more) pv_issue<KS + 1, D>(nxt, va);
+    lds_wait_bind<more ? 2 * (D / 32) : 0, D / 32>(cur);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 a = {cur[0][db][0], cur[0][db][1], cur[0][db][2], cur[0][db][3],
+                          cur[1][db][0], cur[1][db][1], cur[1][db][2], cur[1][db][3]};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+            oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][KS], oacc[rb][db], 0, 0, 0);
+    }
+}
+template <int D, int NKS, int RB, int... KS>
+__device__ inline void pv_steps(f32x16 (&oacc)[RB][D / 32], const bf16x8 (&pb)[RB][NKS],
+                                bf16x4 (&f)[2][2][D / 32], const uint32_t (&va)[2][D / 32],
+                                std::integer_sequence<int, KS...>) {
+    (pv_step<KS, D, NKS, RB>(oacc, pb, f[KS & 1], f[(KS + 1) & 1], va), ...);
+}
+// NKS key steps of 16 keys: the whole tile.
+template <int D, int NKS, int RB>
+__device__ inline void pv_tile(f32x16 (&oacc)[RB][D / 32], const bf16x8 (&pb)[RB][NKS],
+                               const uint32_t (&va)[2][D / 32]) {
+    bf16x4 f[2][2][D / 32];
+    pv_issue<0, D>(f[0], va);
+    pv_steps<D, NKS, RB>(oacc, pb, f, va, std::make_integer_sequence<int, NKS>{});
 }
 // Wait until at most N vector-memory operations of this wave are in flight
 // (s_waitcnt vmcnt(N)), leaving the LDS/scalar and export counters
@@ -78,6 +159,24 @@ template <int CPR>
 __device__ inline int swz(int key) {
     if (CPR == 16) return ((key & 3) << 2) | ((key >> 2) & 3);
     return (((key >> 1) & 1) << 2) | ((key >> 2) & 3);
+}
+
+// Lane offsets (bytes, within a V tile) of the transposing reads of key step
+// 0 used by pv_tile.  swz only depends on the low 4 bits of the key, so key
+// step ks is these offsets plus 16 rows.
+template <int D>
+__device__ inline void pv_lane_offsets(uint32_t (&voff)[2][D / 32], int lane) {
+    constexpr int CPR = D / 8;
+    const int i = lane & 15;
+    const int key = 4 * (lane >> 5) + (i >> 2);
+    const int d = 16 * ((lane >> 4) & 1) + 4 * (i & 3);  // feature within a 32-block
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k = key + 8 * h;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            voff[h][db] = (uint32_t)(k * D * 2 + (d & 7) * 2 + (((db * 4 + (d >> 3)) ^ swz<CPR>(k)) * 16));
+    }
 }
 __device__ inline void buf_store_b64(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte_off, 0, 0);

@@ -27,8 +27,11 @@
 //     bank conflicts on the 64-bank LDS.
 //   * Per wave, the scores of key tile t+1 are issued on the matrix cores in
 //     the same basic block that forms tile t's weights on the vector ALUs.
-//     K therefore runs one tile ahead of V: LDS holds a ring of KST K tiles
-//     and a ring of 2 V tiles.
+//     K therefore runs one tile ahead of V: LDS holds two K tiles (t+1 being
+//     read, t+2 loading) and two V tiles (t being read, t+1 loading).  The
+//     loop is unrolled by two so both ring slots are compile-time offsets.
+//   * The V^T reads are issued as inline assembly (see ds_read_tr16_asm) so
+//     the compiler does not stall them behind the tile prefetches.
 //   * Softmax in the exp2 domain: the row maximum is taken on raw scores,
 //     one FMA forms score * scale * log2(e) - base, and the base is only
 //     moved when a row's maximum grows by more than 8 (so weights stay
@@ -122,7 +125,7 @@ __device__ inline void score_tile(STile<BN, RB>& st, const unsigned char* kst,
     }
 }
 
-template <int D, bool CAUSAL, int RB, int BN, int WAVES, int KST, int WPE>
+template <int D, bool CAUSAL, int RB, int BN, int WAVES, int WPE>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
 prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                     const bf16* __restrict__ V, bf16* __restrict__ O, int B, int H_q, int H_kv,
@@ -134,11 +137,10 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     constexpr int TILE = BN * ROWB;               // bytes of one K or V tile
     constexpr int NLD = TILE / (1024 * WAVES);    // 1 KiB loads per wave per tile
     static_assert(NLD * 1024 * WAVES == TILE, "tile must split into 1 KiB wave loads");
-    static_assert(KST >= 3, "K ring needs t+1 in use and t+2 in flight");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[(KST + 2) * TILE];
-    unsigned char* const kring = smem;               // KST K tiles
-    unsigned char* const vring = smem + KST * TILE;  // 2 V tiles
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];
+    unsigned char* const kring = smem;             // 2 K tiles
+    unsigned char* const vring = smem + 2 * TILE;  // 2 V tiles
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -198,10 +200,11 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             buf_load_lds16(r, dst + blk * 1024, (uint32_t)(j0 + row) * ROWB + logical * 16);
         }
     };
-    auto issue_k = [&](int t) { issue(rK, kring + (t % KST) * TILE, t); };
+    auto issue_k = [&](int t) { issue(rK, kring + (t & 1) * TILE, t); };
     auto issue_v = [&](int t) { issue(rV, vring + (t & 1) * TILE, t); };
 
-    // Prologue: K(0), V(0), K(1).  Iteration t then issues K(t+2), V(t+1).
+    // Prologue: K(0), V(0), K(1).  Step t then issues K(t+2) into K(t)'s slot
+    // and V(t+1) into V(t-1)'s slot, both read for the last time in step t-1.
     if (n_kt > 0) {
         issue_k(0);
         issue_v(0);
@@ -220,22 +223,22 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-    // Lane constants of the transposing V read and the half exchange.
-    const int xaddr = 4 * (lane ^ 32);
-    const int tr_i = lane & 15;
-    const int tr_key = 4 * hi + (tr_i >> 2);                  // + 16 ks + 8 r
-    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);  // feature within a 32-block
-    const int tr_c = tr_d >> 3;                                // its chunk (+ 4 db)
-    const int dbyte = (tr_d & 7) * 2;                          // byte within the chunk
+    const int xaddr = 4 * (lane ^ 32);  // half exchange
+    uint32_t voff[2][D / 32];           // V^T read offsets within a tile
+    pv_lane_offsets<D>(voff, lane);
 
-    STile<BN, RB> s_cur, s_next;
+    STile<BN, RB> s_a, s_b;  // scores of the current and the next tile, alternating
     if (n_kt > 0) {
         wait_vmem_all();
         __syncthreads();
-        if (0 < wave_kv_end) score_tile<D, BN, RB>(s_cur, kring, qf, l32, hi);
+        if (0 < wave_kv_end) score_tile<D, BN, RB>(s_a, kring, qf, l32, hi);
     }
 
-    for (int t = 0; t < n_kt; ++t) {
+    // Step t with PAR = t & 1 known at compile time: K(t+1) sits in slot
+    // 1 - PAR, V(t) in slot PAR.  s_cur holds the scores of tile t, s_next
+    // receives those of tile t+1.
+    auto step = [&](int t, auto par, STile<BN, RB>& s_cur, STile<BN, RB>& s_next) {
+        constexpr int PAR = decltype(par)::value;
         const int j0 = t * BN;
         // K(t+1) and V(t), issued one iteration ago, must be complete in LDS
         // (for every wave's loads), and every wave must be done reading K(t-1)
@@ -244,7 +247,7 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         __syncthreads();
         if (t + 2 < n_kt) issue_k(t + 2);
         if (t + 1 < n_kt) issue_v(t + 1);
-        if (j0 >= wave_kv_end) continue;  // this and all later tiles are above the diagonal
+        if (j0 >= wave_kv_end) return;  // this and all later tiles are above the diagonal
 
         // Per row block: mask, base update.
 #pragma unroll
@@ -293,7 +296,7 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         // cores while the weights of tile t are formed on the vector ALUs,
         // then O += P V for tile t.  (After the wave's last tile the
         // next-scores read a stale stage and are discarded.)
-        score_tile<D, BN, RB>(s_next, kring + ((t + 1) % KST) * TILE, qf, l32, hi);
+        score_tile<D, BN, RB>(s_next, kring + (1 - PAR) * TILE, qf, l32, hi);
 
         bf16x8 pb[RB][BN / 16];
 #pragma unroll
@@ -321,30 +324,19 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             l_run[rb] += ps0 + ps1;
         }
 
-        // O^T += V^T P^T.  Lane (feature d, half hi) needs V for keys
-        // 16ks + 4hi + {0..3} and 16ks + 8 + 4hi + {0..3}, the keys its P
-        // operand holds; two transposing reads deliver exactly those, and
-        // each V fragment feeds RB MFMAs.
-        const unsigned char* vst = vring + (t & 1) * TILE;
+        // O^T += V^T P^T for tile t.
+        const uint32_t vbase = lds_u32(vring + PAR * TILE);
+        uint32_t va[2][D / 32];
 #pragma unroll
-        for (int ks = 0; ks < BN / 16; ++ks) {
-            const int k_lo = ks * 16 + tr_key;
-            const int k_hi = k_lo + 8;
-            const unsigned char* vlo = vst + k_lo * ROWB + dbyte;
-            const unsigned char* vhi = vst + k_hi * ROWB + dbyte;
-            const int sw_lo = swz<CPR>(k_lo), sw_hi = swz<CPR>(k_hi);
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int dchunk = db * 4 + tr_c;
-                const bf16x4 lo = lds_read_tr16(vlo + ((dchunk ^ sw_lo) * 16));
-                const bf16x4 h4 = lds_read_tr16(vhi + ((dchunk ^ sw_hi) * 16));
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][ks], oacc[rb][db], 0, 0, 0);
-            }
+            for (int db = 0; db < D / 32; ++db) va[h][db] = vbase + voff[h][db];
         }
-        s_cur = s_next;
+        pv_tile<D, BN / 16, RB>(oacc, pb, va);
+    };
+    for (int t = 0; t < n_kt; t += 2) {
+        step(t, std::integral_constant<int, 0>{}, s_a, s_b);
+        if (t + 1 < n_kt) step(t + 1, std::integral_constant<int, 1>{}, s_b, s_a);
     }
 
     // Epilogue: O = O_acc / l, rounded once to bf16.  Rows past T_q fall
@@ -368,12 +360,12 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
 }
 
-template <int D, bool CAUSAL, int RB, int BN, int WAVES, int KST, int WPE>
+template <int D, bool CAUSAL, int RB, int BN, int WAVES, int WPE>
 hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
     constexpr int BM = 32 * RB * WAVES;
     const int n_qt = (a.T_q + BM - 1) / BM;
     const long long grid = (long long)a.B * a.H_q * n_qt;
-    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, RB, BN, WAVES, KST, WPE>, dim3((unsigned)grid),
+    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, RB, BN, WAVES, WPE>, dim3((unsigned)grid),
                          dim3(64 * WAVES), 0, s, static_cast<const bf16*>(a.q),
                          static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                          static_cast<bf16*>(a.o), a.B, a.H_q, a.H_kv, a.T_q, a.T_kv, n_qt, a.c_log2,
@@ -386,13 +378,13 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
 
 // Large problems (at least two 256-row workgroups per CU): 8 waves, one
 // workgroup per CU.  Otherwise 4 waves, two workgroups per CU.  Both use
-// 80 KiB of LDS (K ring of 3, V ring of 2).
+// 64 KiB of LDS (two K and two V tiles).
 template <int D, bool CAUSAL>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
     const long long wg_big = (long long)a.B * a.H_q * ((a.T_q + 255) / 256);
     const bool big = PF_FORCE == 2 || (PF_FORCE == 0 && wg_big >= 512);
-    if (big) return launch_cfg<D, CAUSAL, 1, 64, 8, 3, 2>(a, s);
-    return launch_cfg<D, CAUSAL, 1, 64, 4, 3, 2>(a, s);
+    if (big) return launch_cfg<D, CAUSAL, 1, 64, 8, 2>(a, s);
+    return launch_cfg<D, CAUSAL, 1, 64, 4, 2>(a, s);
 }
 
 }  // namespace
