@@ -179,6 +179,73 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
         print(f"wrote profiles/{name}.md")
 
 
+PAGE_SIZE = 16
+
+
+def time_paged_decode(abi, torch, wd, kd, vd, qd, od_contig, stream, dev, warmup, settle, steps):
+    """The decode workload over a paged cache: the same K/V values scattered
+    into shuffled pools of 16-token pages (64 * 256 pages of 4 KiB per kv
+    head), one block-table row per sequence.  Returns the JSON object."""
+    B, H_kv, T, D = wd.B, wd.H_kv, wd.T_kv, wd.D
+    per = T // PAGE_SIZE
+    n_pages = B * per
+    g = torch.Generator(device="cpu").manual_seed(5005)
+    perm = torch.randperm(n_pages, generator=g).to(dev)
+    def scatter(x):
+        logical = x.view(B, H_kv, per, PAGE_SIZE, D).permute(0, 2, 1, 3, 4).reshape(n_pages, H_kv, PAGE_SIZE, D)
+        pool = torch.empty_like(logical)
+        pool[perm] = logical
+        return pool
+    kpool, vpool = scatter(kd), scatter(vd)
+    table = perm.view(B, per).to(torch.int32).contiguous()
+    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+    q2 = qd.view(B, wd.H_q, D)
+    o2 = torch.empty_like(q2)
+    ws_bytes = abi.attn_fwd_decode_paged_workspace_bytes(B, wd.H_q, H_kv, D, PAGE_SIZE, per, 0)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def run():
+        abi.attn_fwd_decode_paged(q2, kpool, vpool, o2, table, lens, B, wd.H_q, H_kv, D, PAGE_SIZE,
+                                  n_pages, per, wd.scale, abi.ATTN_BF16, 0, ws, ws_bytes, stream)
+
+    log("paged decode: warmup")
+    t_settle = time.perf_counter() + settle
+    done = 0
+    while done < warmup or time.perf_counter() < t_settle:
+        run()
+        done += 1
+        if done % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / steps
+    nbytes = wd.bytes() + table.numel() * 4 + lens.numel() * 4
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    same = None
+    if od_contig is not None:
+        same = bool(torch.equal(o2, od_contig.view(B, wd.H_q, D)))
+    log(f"paged decode: {avg * 1e3:.1f} us, {gbs:.1f} GB/s")
+    return {
+        "metric": "paged-KV decode KV-read GB/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "config": {"workload": f"decode B={B} H_q={wd.H_q} H_kv={H_kv} T_kv={T} D={D} bf16, "
+                               f"pages of {PAGE_SIZE} tokens in a shuffled pool of {n_pages}",
+                   "bytes": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128, paged>",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_call_us": round(avg * 1e3, 2), "min_call_us": round(min(ms) * 1e3, 2)},
+        "equals_contiguous_decode": same,
+    }
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         # python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR COPY_MIB "commands"
@@ -191,8 +258,9 @@ def main():
     ap.add_argument("--settle", type=float, default=1.0,
                     help="minimum seconds of untimed warm-up (GPU clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one half of the step (for profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "paged"], default=None,
+                    help="time one part only (for profiling runs)")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV decode line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -229,6 +297,7 @@ def main():
 
     do_p = args.only in (None, "prefill")
     do_d = args.only in (None, "decode")
+    do_pg = args.only == "paged" or (args.only is None and not args.no_paged)
 
     def run_prefill():
         abi.attn_fwd_prefill(qp, kp, vp, op, wp.B, wp.H_q, wp.H_kv, wp.T_q, wp.T_kv, wp.D, wp.causal,
@@ -278,6 +347,11 @@ def main():
     d_avg = sum(d_ms) / K
     p_tflops = wp.flops() / (p_avg * 1e-3) / 1e12 if do_p else None
     d_gbs = wd.bytes() / (d_avg * 1e-3) / 1e9 if do_d else None
+
+    paged = None
+    if do_pg:
+        paged = time_paged_decode(abi, torch, wd, kd, vd, qd, od if do_d else None, stream, dev,
+                                  args.warmup, args.settle, K)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -343,6 +417,8 @@ def main():
                 "min_call_us": round(min(d_ms) * 1e3, 2),
             },
         }
+    if paged is not None:
+        result["paged_decode"] = paged
     if not args.no_cpu_baseline and do_p:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline()

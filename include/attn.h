@@ -128,6 +128,48 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
                               int causal, float scale, int dtype, int num_splits,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode over a paged KV cache (the serving form of decode; Ch. 11 page,
+ * section 11.11: the KV cache is kept in fixed-size pages of 16 tokens, and a
+ * block table maps (request, token / 16) to a physical page that the
+ * attention kernel loads through one indirection).  Same arithmetic, split
+ * plan and workspace rules as attn_fwd_decode (bf16 only).
+ *
+ *   q            device [B][H_q][D]: one query token per sequence
+ *   k_pages,     device [num_pages][H_kv][page_size][D] each: the K and V
+ *   v_pages      pools; physical page p holds rows 0..page_size-1 of one
+ *                logical page of some sequence, for every kv head
+ *   o            device [B][H_q][D], fully overwritten
+ *   block_table  device int32 [B][max_pages]: token j of sequence b is row
+ *                j % page_size of page block_table[b][j / page_size]; only
+ *                entries below ceil(seq_lens[b] / page_size) are read
+ *   seq_lens     device int32 [B]: keys of sequence b
+ *   page_size    a power of two, 16 ... 65536
+ *   num_pages    pages in each pool (>= 1)
+ *   max_pages    columns of block_table (>= 1); max_pages * page_size is the
+ *                longest sequence (<= 2^30) and sizes the split plan
+ *   num_splits, workspace, workspace_bytes: as for attn_fwd_decode, with
+ *                T_kv = max_pages * page_size
+ *                (attn_fwd_decode_paged_workspace_bytes gives the size)
+ *
+ * Device-side values are not checked on the host; instead, with no fault in
+ * any case: seq_lens[b] is clamped to [0, max_pages * page_size]; a sequence
+ * of length 0 gets O = 0; a block id outside [0, num_pages) reads as a page
+ * of zeros.  Pages are read only up to the sequence's last key.
+ * Pointer checks: q, k_pages, v_pages, o and the workspace 16-byte aligned,
+ * block_table and seq_lens 4-byte aligned; o and the workspace may overlap
+ * no input.  dtype must be ATTN_BF16.
+ */
+attn_status_t attn_fwd_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                    void* o, const int* block_table, const int* seq_lens, int B,
+                                    int H_q, int H_kv, int D, int page_size, int num_pages,
+                                    int max_pages, float scale, int dtype, int num_splits,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_decode_paged needs (0 if none or invalid sizes). */
+size_t attn_fwd_decode_paged_workspace_bytes(int B, int H_q, int H_kv, int D, int page_size,
+                                             int max_pages, int num_splits);
+
 /* Workspace bytes attn_fwd_decode needs for these sizes (num_splits as
  * passed to attn_fwd_decode, 0 = default).  Returns 0 when no workspace is
  * needed (one split, or dtype ATTN_F32) and for invalid sizes. */

@@ -135,3 +135,47 @@ def test_decode_workspace_too_small_by_one_byte():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         A.load_library(tmp_path / "libattn.so")
+
+
+# --- paged decode -------------------------------------------------------------------
+TP, SP = 0x60000000, 0x70000000  # fake block table / seq_lens addresses
+
+
+def paged(q=QP, k=KP, v=VP, o=OP, table=TP, lens=SP, B=2, H_q=8, H_kv=2, D=128, ps=16,
+          num_pages=64, max_pages=8, scale=0.1, dtype=BF16, splits=0, ws=WP, ws_bytes=1 << 30):
+    return A.attn_fwd_decode_paged(q, k, v, o, table, lens, B, H_q, H_kv, D, ps, num_pages,
+                                   max_pages, scale, dtype, splits, ws, ws_bytes, None, check=False)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), SHAPE), (dict(H_q=0), SHAPE), (dict(H_q=6, H_kv=4), SHAPE),
+    (dict(num_pages=0), SHAPE), (dict(max_pages=0), SHAPE),
+    (dict(max_pages=1 << 20, ps=4096), SHAPE),
+    (dict(ps=8), UNSUP), (dict(ps=24), UNSUP), (dict(ps=1 << 17), UNSUP),
+    (dict(dtype=F32), UNSUP), (dict(D=96), UNSUP), (dict(splits=1025), UNSUP),
+    (dict(scale=float("nan")), SCALE),
+    (dict(q=0), NULL), (dict(table=0), NULL), (dict(lens=0), NULL), (dict(v=0), NULL),
+    (dict(q=QP + 8), ALIGN), (dict(table=TP + 2), ALIGN), (dict(lens=SP + 1), ALIGN),
+    (dict(o=TP), ALIAS), (dict(o=KP + 16), ALIAS), (dict(ws=SP, max_pages=64), ALIAS),
+    (dict(ws=0, max_pages=64), WS), (dict(ws_bytes=15, max_pages=64), WS),
+])
+def test_paged_rejects(kw, want):
+    assert paged(**kw) == want
+
+
+def test_paged_table_and_lens_only_need_4_byte_alignment():
+    # 4-byte aligned table / lengths pass validation (checked with B = 0: no launch)
+    assert paged(B=0, table=TP + 4, lens=SP + 4) == OK
+    assert paged(B=0, q=0, k=0, v=0, o=0, table=0, lens=0) == OK
+
+
+def test_paged_workspace_size():
+    # one split (enough groups) -> no workspace; few groups -> split over max_pages * ps keys
+    assert A.attn_fwd_decode_paged_workspace_bytes(64, 32, 8, 128, 16, 256, 0) == 0
+    n = A.attn_fwd_decode_paged_workspace_bytes(1, 32, 8, 128, 16, 256, 0)
+    assert n == 1 * 32 * A.attn_fwd_decode_default_splits(1, 32, 8, 4096, 128) * 130 * 4
+    assert A.attn_fwd_decode_paged_workspace_bytes(2, 8, 2, 128, 16, 8, 4) == \
+        A.attn_fwd_decode_workspace_bytes(2, 8, 2, 128, 128, BF16, 4)
+    assert A.attn_fwd_decode_paged_workspace_bytes(2, 8, 2, 128, 12, 8, 4) == 0  # bad page size
+    need = A.attn_fwd_decode_paged_workspace_bytes(2, 8, 2, 128, 16, 64, 0)
+    assert need > 0 and paged(max_pages=64, ws_bytes=need - 1) == WS

@@ -36,6 +36,8 @@ EXPORTED = (
     "attn_fwd_decode",
     "attn_fwd_decode_workspace_bytes",
     "attn_fwd_decode_default_splits",
+    "attn_fwd_decode_paged",
+    "attn_fwd_decode_paged_workspace_bytes",
     "attn_status_string",
     "attn_abi_version",
     "attn_last_hip_error",
@@ -76,6 +78,11 @@ def load_library(path: Path | str | None = None):
     lib.attn_fwd_decode_workspace_bytes.restype = sz
     lib.attn_fwd_decode_default_splits.argtypes = [i, i, i, i, i]
     lib.attn_fwd_decode_default_splits.restype = i
+    lib.attn_fwd_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp,
+                                          sz, vp]
+    lib.attn_fwd_decode_paged.restype = i
+    lib.attn_fwd_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.attn_fwd_decode_paged_workspace_bytes.restype = sz
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -127,6 +134,24 @@ def attn_fwd_decode(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, causal, scale, dtype
     if check:
         _check(st, "attn_fwd_decode")
     return st
+
+
+def attn_fwd_decode_paged(q, k_pages, v_pages, o, block_table, seq_lens, B, H_q, H_kv, D,
+                          page_size, num_pages, max_pages, scale, dtype, num_splits, workspace,
+                          workspace_bytes, stream=None, check=True) -> int:
+    lib = load_library()
+    st = lib.attn_fwd_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o),
+                                   _ptr(block_table), _ptr(seq_lens), B, H_q, H_kv, D, page_size,
+                                   num_pages, max_pages, float(scale), dtype, num_splits,
+                                   _ptr(workspace), workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "attn_fwd_decode_paged")
+    return st
+
+
+def attn_fwd_decode_paged_workspace_bytes(B, H_q, H_kv, D, page_size, max_pages, num_splits=0) -> int:
+    return int(load_library().attn_fwd_decode_paged_workspace_bytes(B, H_q, H_kv, D, page_size,
+                                                                     max_pages, num_splits))
 
 
 def attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, dtype, num_splits=0) -> int:

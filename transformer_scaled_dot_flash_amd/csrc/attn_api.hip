@@ -109,6 +109,31 @@ size_t decode_ws_bytes(int B, int H_q, int D, const SplitPlan& p) {
     return (size_t)B * H_q * p.n_splits * (D + 2) * sizeof(float);
 }
 
+// Paged cache: page_size a power of two in [16, 65536]; returns log2 or -1.
+int page_shift_of(int page_size) {
+    if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1))) return -1;
+    int s = 0;
+    while ((1 << s) < page_size) ++s;
+    return s;
+}
+
+attn_status_t check_paged_params(int B, int H_q, int H_kv, int D, int page_size, int num_pages,
+                                 int max_pages, int dtype, float scale, int num_splits) {
+    if (B < 0 || H_q <= 0 || H_kv <= 0 || num_pages <= 0 || max_pages <= 0) return ATTN_ERR_INVALID_SHAPE;
+    if (H_q % H_kv != 0) return ATTN_ERR_INVALID_SHAPE;
+    if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (page_shift_of(page_size) < 0) return ATTN_ERR_UNSUPPORTED;
+    if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_SCALE;
+    // Key positions are 32-bit and one page of one kv head is addressed with
+    // 32-bit offsets.
+    if ((long long)max_pages * page_size > (1LL << 30)) return ATTN_ERR_INVALID_SHAPE;
+    const long long waves = (long long)B * H_kv * ((H_q / H_kv + 31) / 32) * kMaxSplits;
+    if (waves / 4 > 0x7fffffffLL || (long long)B * H_q > 0x7fffffffLL) return ATTN_ERR_INVALID_SHAPE;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,7 +154,7 @@ attn_status_t attn_fwd_prefill(const void* q, const void* k, const void* v, void
     st = check_tensors(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, dtype);
     if (st != ATTN_OK) return st;
 
-    attn::PrefillArgs a;
+    attn::PrefillArgs a{};
     a.q = q;
     a.k = k;
     a.v = v;
@@ -166,7 +191,7 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (dtype == ATTN_F32) {
-        attn::PrefillArgs a;
+        attn::PrefillArgs a{};
         a.q = q;
         a.k = k;
         a.v = v;
@@ -195,7 +220,7 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
         overlaps(workspace, need, k, nkv) || overlaps(workspace, need, v, nkv))
         return ATTN_ERR_ALIAS;
 
-    attn::DecodeArgs a;
+    attn::DecodeArgs a{};
     a.q = q;
     a.k = k;
     a.v = v;
@@ -224,6 +249,65 @@ size_t attn_fwd_decode_workspace_bytes(int B, int H_q, int H_kv, int T_kv, int D
 int attn_fwd_decode_default_splits(int B, int H_q, int H_kv, int T_kv, int D) {
     if (check_params(B, H_q, H_kv, 1, T_kv, D, ATTN_BF16, 1.0f) != ATTN_OK) return 0;
     return plan_splits(B, H_q, H_kv, T_kv, 0).n_splits;
+}
+
+attn_status_t attn_fwd_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                    void* o, const int* block_table, const int* seq_lens, int B,
+                                    int H_q, int H_kv, int D, int page_size, int num_pages,
+                                    int max_pages, float scale, int dtype, int num_splits,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    attn_status_t st = check_paged_params(B, H_q, H_kv, D, page_size, num_pages, max_pages, dtype,
+                                          scale, num_splits);
+    if (st != ATTN_OK) return st;
+    if (B == 0) return ATTN_OK;
+    if (!q || !k_pages || !v_pages || !o || !block_table || !seq_lens) return ATTN_ERR_NULL_PTR;
+    if (misaligned(q) || misaligned(k_pages) || misaligned(v_pages) || misaligned(o) ||
+        (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+        return ATTN_ERR_ALIGNMENT;
+    const int T_max = max_pages * page_size;
+    const SplitPlan p = plan_splits(B, H_q, H_kv, T_max, num_splits);
+    const size_t need = decode_ws_bytes(B, H_q, D, p);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+    if (need > 0 && misaligned(workspace)) return ATTN_ERR_ALIGNMENT;
+    const size_t nq = (size_t)B * H_q * D * 2;
+    const size_t npool = (size_t)num_pages * H_kv * page_size * D * 2;
+    const size_t nbt = (size_t)B * max_pages * 4, nsl = (size_t)B * 4;
+    const void* ins[] = {q, k_pages, v_pages, block_table, seq_lens};
+    const size_t lens[] = {nq, npool, npool, nbt, nsl};
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(o, nq, ins[i], lens[i]) || overlaps(workspace, need, ins[i], lens[i]))
+            return ATTN_ERR_ALIAS;
+    if (overlaps(workspace, need, o, nq)) return ATTN_ERR_ALIAS;
+
+    attn::DecodeArgs a{};
+    a.q = q;
+    a.k = k_pages;
+    a.v = v_pages;
+    a.o = o;
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.T_kv = T_max;
+    a.D = D;
+    positive_scale(scale, &a.c_log2, &a.neg_q);
+    a.n_splits = p.n_splits;
+    a.keys_per_split = p.keys_per_split;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_o + (size_t)B * H_q * p.n_splits * D;
+    a.paged.block_table = block_table;
+    a.paged.seq_lens = seq_lens;
+    a.paged.max_pages = max_pages;
+    a.paged.page_shift = page_shift_of(page_size);
+    a.paged.num_pages = num_pages;
+    return hip_status(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_fwd_decode_paged_workspace_bytes(int B, int H_q, int H_kv, int D, int page_size,
+                                             int max_pages, int num_splits) {
+    if (check_paged_params(B, H_q, H_kv, D, page_size, 1, max_pages, ATTN_BF16, 1.0f, num_splits) !=
+        ATTN_OK)
+        return 0;
+    return decode_ws_bytes(B, H_q, D, plan_splits(B, H_q, H_kv, max_pages * page_size, num_splits));
 }
 
 const char* attn_status_string(int status) {

@@ -25,6 +25,17 @@
 // straight into its own LDS ring of kStages tiles with 16-byte buffer loads
 // (each 1 KiB load covers four whole rows), keeping kStages - 1 tiles in
 // flight while it consumes one; waves never synchronise with each other.
+//
+// Paged KV cache (the serving form; Ch. 11 page, section 11.11 on KV-cache
+// pages of 16 tokens and the block table that maps (request, token / 16) to
+// a physical block): K and V live in pools of pages [num_pages][H_kv]
+// [page_size][D]; token j of sequence b is row j % page_size of page
+// block_table[b][j / page_size].  The split kernel is the same; only the
+// tile loads change: every 1 KiB load covers rows of one page, addressed
+// through a buffer resource built for that page (so the pool may be of any
+// size, rows past the sequence's length read as zero, and a block id outside
+// the pool reads as a page of zeros instead of faulting).  The block ids of
+// 64 consecutive pages are held one per lane and picked with v_readlane.
 #include "kernel_common.h"
 
 namespace attn {
@@ -49,11 +60,11 @@ __device__ inline void wait_tiles_ahead(int ahead) {
     }
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ ws_o, float* __restrict__ ws_ml, int H_q, int H_kv,
-    int T_kv, int n_splits, int kps, int n_hb, float c, int neg_q) {
+    int T_kv, int n_splits, int kps, int n_hb, float c, int neg_q, PagedKV pg) {
     constexpr int CPR = D / 8;
     constexpr int ROWB = D * 2;
     constexpr int TILE = kBN * ROWB;  // bytes of one K or V tile
@@ -78,26 +89,73 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const bool valid = gi < G;
     const int hq = hk * G + gi;
 
+    // Keys of this sequence: T_kv, or its own length in the paged form
+    // (clamped to the block table's capacity T_kv; 0 gives O = 0).
+    int seq_len = T_kv;
+    if constexpr (PAGED) seq_len = min(max(pg.seq_lens[b], 0), T_kv);
     const int k0 = split * kps;
-    const int k1 = min(T_kv, k0 + kps);
-    const int n_t = (k1 - k0 + kBN - 1) / kBN;
+    const int k1 = min(seq_len, k0 + kps);
+    const int n_t = k1 > k0 ? (k1 - k0 + kBN - 1) / kBN : 0;
 
-    // This split's keys only: loads past k1 read as zero.
-    const uint32_t split_bytes = (uint32_t)(k1 - k0) * ROWB;
-    const auto rK = make_rsrc(K + ((size_t)unit * T_kv + k0) * D, split_bytes);
-    const auto rV = make_rsrc(V + ((size_t)unit * T_kv + k0) * D, split_bytes);
+    // Contiguous cache: this split's keys only; loads past k1 read as zero.
+    const uint32_t split_bytes = PAGED ? 0u : (uint32_t)(k1 - k0) * ROWB;
+    const size_t split_base = PAGED ? 0 : ((size_t)unit * T_kv + k0) * D;
+    const auto rK = make_rsrc(K + split_base, split_bytes);
+    const auto rV = make_rsrc(V + split_base, split_bytes);
+
+    // Paged cache: block ids of pages [id_base, id_base + 64), one per lane.
+    int id_base = -(1 << 30), ids = 0;
+    const int page_size = 1 << pg.page_shift;
+    auto block_of = [&](int page) {
+        if (page - id_base >= 64 || page < id_base) {
+            // Rare (every 64 pages): the wait also drains the tile loads.
+            const auto rT = make_rsrc(pg.block_table + (size_t)b * pg.max_pages,
+                                      (uint32_t)pg.max_pages * 4);
+            id_base = page;
+            ids = __builtin_amdgcn_raw_buffer_load_b32(rT, (page + lane) * 4, 0, 0);
+            wait_vmem_all();
+        }
+        return __builtin_amdgcn_readlane(ids, page - id_base);
+    };
+    // Rows [page * page_size, seq_len) of one page of a pool.
+    auto page_rsrc = [&](const bf16* pool, int page, int blk) {
+        const int rows = min(page_size, seq_len - (page << pg.page_shift));
+        const bool ok = rows > 0 && (unsigned)blk < (unsigned)pg.num_pages;
+        const bf16* base = pool + ((size_t)(ok ? blk : 0) * H_kv + hk) * ((size_t)page_size * D);
+        return make_rsrc(base, ok ? (uint32_t)rows * ROWB : 0u);
+    };
 
     auto issue = [&](int t) {
         unsigned char* kst = smem + (t % kStages) * 2 * TILE;
         unsigned char* vst = kst + TILE;
+        if constexpr (PAGED) {
+            // A 32-key tile spans one page, or two when page_size == 16.
+            const int key_t = k0 + t * kBN;
+            const int pa = key_t >> pg.page_shift, pb = (key_t + 16) >> pg.page_shift;
+            const int ba = block_of(pa), bb = block_of(pb);
+            const auto kA = page_rsrc(K, pa, ba), vA = page_rsrc(V, pa, ba);
+            const auto kB = page_rsrc(K, pb, bb), vB = page_rsrc(V, pb, bb);
 #pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const int p = n * 64 + lane;
-            const int row = p / CPR;
-            const int logical = (p % CPR) ^ swz<CPR>(row);
-            const uint32_t boff = (uint32_t)(t * kBN + row) * ROWB + logical * 16;
-            buf_load_lds16(rK, kst + n * 1024, boff);
-            buf_load_lds16(rV, vst + n * 1024, boff);
+            for (int n = 0; n < NLD; ++n) {
+                const int p = n * 64 + lane;
+                const int row = p / CPR;
+                const int logical = (p % CPR) ^ swz<CPR>(row);
+                const bool second = ((key_t + n * (64 / CPR)) >> pg.page_shift) != pa;
+                const uint32_t boff =
+                    (uint32_t)((key_t + row) & (page_size - 1)) * ROWB + logical * 16;
+                buf_load_lds16(second ? kB : kA, kst + n * 1024, boff);
+                buf_load_lds16(second ? vB : vA, vst + n * 1024, boff);
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NLD; ++n) {
+                const int p = n * 64 + lane;
+                const int row = p / CPR;
+                const int logical = (p % CPR) ^ swz<CPR>(row);
+                const uint32_t boff = (uint32_t)(t * kBN + row) * ROWB + logical * 16;
+                buf_load_lds16(rK, kst + n * 1024, boff);
+                buf_load_lds16(rV, vst + n * 1024, boff);
+            }
         }
     };
 
@@ -207,8 +265,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     if (!valid) return;
     const size_t row = (size_t)(b * H_q + hq);
     if (n_splits == 1) {
-        // The single split covers every key: normalise and write O directly.
-        const float inv = 1.f / l_tot;
+        // The single split covers every key: normalise and write O directly
+        // (an empty paged sequence has l = 0 and gets O = 0).
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         bf16* orow = O + row * D + 4 * hi;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -249,32 +308,33 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     const float* ml = ws_ml + row * n_splits * 2;
     float m = -INFINITY;
     for (int s = 0; s < n_splits; ++s) m = fmaxf(m, ml[2 * s]);
+    if (m == -INFINITY) m = 0.f;  // every split empty (a paged sequence of length 0): O = 0
     float L = 0.f;
     float acc[D / 64];
 #pragma unroll
     for (int r = 0; r < D / 64; ++r) acc[r] = 0.f;
     const float* op = ws_o + row * n_splits * D + lane;
     for (int s = 0; s < n_splits; ++s) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * s] - m);
+        const float w = ml[2 * s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[2 * s] - m);
         L += ml[2 * s + 1] * w;
 #pragma unroll
         for (int r = 0; r < D / 64; ++r) acc[r] += w * op[(size_t)s * D + 64 * r];
     }
-    const float inv = 1.f / L;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int r = 0; r < D / 64; ++r) O[row * D + lane + 64 * r] = (bf16)(acc[r] * inv);
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
     const int G = a.H_q / a.H_kv;
     const int n_hb = (G + 31) / 32;
     const long long waves = (long long)a.B * a.H_kv * n_hb * a.n_splits;
-    hipError_t e = launch_kernel(decode_split_kernel<D>, dim3((unsigned)waves), dim3(64), 0, s,
+    hipError_t e = launch_kernel(decode_split_kernel<D, PAGED>, dim3((unsigned)waves), dim3(64), 0, s,
                                  static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                                  static_cast<const bf16*>(a.v), static_cast<bf16*>(a.o), a.ws_o, a.ws_ml,
                                  a.H_q, a.H_kv, a.T_kv, a.n_splits, a.keys_per_split, n_hb, a.c_log2,
-                                 a.neg_q);
+                                 a.neg_q, a.paged);
     if (e != hipSuccess || a.n_splits == 1) return e;
     const long long rows = (long long)a.B * a.H_q;
     return launch_kernel(decode_combine_kernel<D>, dim3((unsigned)rows), dim3(64), 0, s,
@@ -285,7 +345,8 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
-    return a.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+    if (a.paged.block_table) return a.D == 128 ? launch_d<128, true>(a, s) : launch_d<64, true>(a, s);
+    return a.D == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
 }
 
 }  // namespace attn

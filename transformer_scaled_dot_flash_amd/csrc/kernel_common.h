@@ -202,6 +202,15 @@ struct PrefillArgs {
     int neg_q;         // 1 when scale < 0: the kernels flip Q's sign instead
 };
 
+// Paged KV cache of the decode kernel (block_table == nullptr: contiguous).
+struct PagedKV {
+    const int* block_table;  // [B][max_pages] physical page of each logical page
+    const int* seq_lens;     // [B] keys of each sequence
+    int max_pages;           // columns of block_table
+    int page_shift;          // log2(page_size)
+    int num_pages;           // pages in each pool
+};
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -214,6 +223,7 @@ struct DecodeArgs {
     int keys_per_split;  // multiple of 32
     float* ws_o;         // [B][H_q][n_splits][D]  unnormalised partial outputs
     float* ws_ml;        // [B][H_q][n_splits][2]  (running max in log2 units, sum)
+    PagedKV paged;       // paged cache (T_kv = max_pages * page_size), or all zero
 };
 
 // Launchers return the HIP status of the launch call itself.

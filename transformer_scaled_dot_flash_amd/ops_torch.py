@@ -66,3 +66,35 @@ def decode(q, k, v, scale: float, num_splits: int = 0, workspace=None, out=None,
     _abi.attn_fwd_decode(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, False, scale, _dtype_code(q),
                          num_splits, ws, ws_bytes, s)
     return o
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float, num_splits: int = 0,
+                 workspace=None, out=None, stream=None):
+    """Decode over a paged KV cache.
+
+    q [B][H_q][1][D] (or [B][H_q][D]) bf16; k_pages, v_pages
+    [num_pages][H_kv][page_size][D] bf16; block_table int32 [B][max_pages];
+    seq_lens int32 [B].  Returns O shaped like q.
+    """
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if k_pages.shape != v_pages.shape or k_pages.dim() != 4:
+        raise ValueError("k_pages and v_pages must both be [num_pages][H_kv][page_size][D]")
+    num_pages, H_kv, page_size, D = k_pages.shape
+    B, H_q = q.shape[0], q.shape[1]
+    max_pages = block_table.shape[1]
+    o = torch.empty_like(q) if out is None else out
+    if workspace is None:
+        n = _abi.attn_fwd_decode_paged_workspace_bytes(B, H_q, H_kv, D, page_size, max_pages,
+                                                       num_splits)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    _abi.attn_fwd_decode_paged(q, k_pages, v_pages, o, block_table, seq_lens, B, H_q, H_kv, D,
+                               page_size, num_pages, max_pages, scale, _dtype_code(q), num_splits,
+                               workspace, ws_bytes, s)
+    return o
