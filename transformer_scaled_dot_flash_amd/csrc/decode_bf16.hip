@@ -41,11 +41,8 @@
 namespace attn {
 namespace {
 
-#ifndef DEC_STAGES
-#define DEC_STAGES 3
-#endif
-constexpr int kBN = 32;      // keys per tile
-constexpr int kStages = DEC_STAGES;   // LDS ring depth per wave
+constexpr int kBN = 32;     // keys per tile
+constexpr int kStages = 2;  // LDS ring depth per wave: one tile in flight while one is consumed
 
 // Wait until tile t of the ring has landed: `ahead` later tiles (PER loads
 // each) may still be in flight.  Loads complete in issue order.
@@ -246,11 +243,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         }
         l_run += ps0 + ps1;
 
-        // O^T += V^T P^T over the tile's two key steps.  All of this wave's
-        // tile loads are drained first: with ~500 waves each streaming its
-        // own key range, keeping about one tile per wave in flight reads HBM
-        // faster (measured 6.1 vs 5.7 TB/s) than letting two stay in flight.
-        wait_vmem_all();
+        // O^T += V^T P^T over the tile's two key steps.  With a contiguous
+        // cache this wave's next tile is drained first (measured 6.1 TB/s
+        // against 5.9 without); with pages it is left in flight (5.8
+        // against 5.3 TB/s): the scattered 4 KiB page reads need the overlap.
+        if constexpr (!PAGED) wait_vmem_all();
         const uint32_t vbase = lds_u32(vst);
         uint32_t va[2][D / 32];
 #pragma unroll
