@@ -100,6 +100,52 @@ attn_status_t attn_fwd_prefill(const void* q, const void* k, const void* v, void
                                int causal, float scale, int dtype, void* stream);
 
 /*
+ * Causal sliding-window attention (Ch. 11 page, section 11.8.4: attend to
+ * the most recent W tokens only, which turns the O(T^2) cost into O(T*W)):
+ * as attn_fwd_prefill with causal = 1, except that query row i (absolute
+ * position p = i + T_kv - T_q) sees only the keys p - window + 1 ... p.  Key
+ * tiles left of every row's window are never visited, tiles that cross a
+ * window edge are masked element by element.
+ *
+ *   window   >= 1 keys; window >= T_kv is plain causal attention
+ *   dtype    ATTN_BF16 only
+ * Requires T_q <= T_kv.  Other arguments as attn_fwd_prefill.
+ */
+attn_status_t attn_fwd_prefill_window(const void* q, const void* k, const void* v, void* o,
+                                      int B, int H_q, int H_kv, int T_q, int T_kv, int D,
+                                      int window, float scale, int dtype, void* stream);
+
+/*
+ * Packed variable-length prefill: B sequences of different lengths in one
+ * call, the flash_attn_varlen_func form of prefill named on the Ch. 11 page
+ * (section 11.8.2).  Layout is token-major and packed:
+ *
+ *   q, o   [total_q][H_q][D];  k, v  [total_k][H_kv][D]
+ *   cu_seqlens_q, cu_seqlens_k   device int32 [B + 1], non-decreasing,
+ *          cu[0] = 0, cu[B] = total: sequence b owns query rows
+ *          cu_seqlens_q[b] ... cu_seqlens_q[b+1] - 1 and key rows
+ *          cu_seqlens_k[b] ... cu_seqlens_k[b+1] - 1
+ *   max_seqlen_q, max_seqlen_k   upper bounds of the per-sequence lengths
+ *          (they size the grid and the 32-bit offset checks; rows of a
+ *          longer sequence beyond max_seqlen_q are not computed)
+ *   total_q, total_k   rows of the packed tensors (used for the overlap
+ *          checks)
+ *   causal, window     per sequence, with bottom-right alignment
+ *          (row i at position i + T_kv_b - T_q_b); window 0 = none, window
+ *          > 0 needs causal
+ *
+ * Device values are not checked on the host.  A query row that sees no key
+ * (an empty key range, or causal with the row before the first key) gets
+ * O = 0.  dtype ATTN_BF16 only; cu arrays 4-byte aligned.  Otherwise as
+ * attn_fwd_prefill.
+ */
+attn_status_t attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o,
+                                      const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                                      int H_q, int H_kv, int D, int total_q, int total_k,
+                                      int max_seqlen_q, int max_seqlen_k, int causal, int window,
+                                      float scale, int dtype, void* stream);
+
+/*
  * Decode forward: one query token per (batch, q head) against T_kv cached
  * keys (Ch. 11 page, section 11.8.2: decode is a vector against the whole
  * KV cache and is memory-bound).  T_q must be 1; `causal` is accepted and

@@ -28,6 +28,13 @@ Sources for each step (cited by page and section):
 * Head mapping for MHA / MQA / GQA: q head h reads kv head h // group_size
   with group_size = H_q / H_kv: Ch. 11 page, section 11.8.1 and the unified
   kernel of section 11.11; AIInfraGuide page, section 9.3.
+* Sliding window (Ch. 11 page, section 11.8.4: each token attends only to
+  the most recent W tokens): with causal masking, row i sees keys j with
+  i + off - W < j <= i + off, i.e. W keys ending at its own position.
+* Packed variable-length batches (the flash_attn_varlen_func prefill form
+  named in section 11.8.2 of the Ch. 11 page): every sequence is an
+  independent attention problem; ``attention_varlen`` slices each one out of
+  the packed token-major tensors and applies the same definition.
 
 Readings where the pages leave a point open:
 
@@ -39,6 +46,9 @@ Readings where the pages leave a point open:
 * Inputs are whatever values the caller passes (float32 values or bfloat16
   values widened exactly); they are converted to float64 and nothing is
   rounded afterwards.  The output is float64.
+* A query row that sees no key at all (only possible in a packed batch: an
+  empty key range, or causal with the row before the first key) has output
+  0; the softmax of an empty row is not defined on the pages.
 
 Layout: Q [B, H_q, T_q, D], K and V [B, H_kv, T_kv, D], O [B, H_q, T_q, D].
 """
@@ -55,14 +65,17 @@ def kv_head_for(h_q: int, H_q: int, H_kv: int) -> int:
     return h_q // group_size
 
 
-def visible(rows: np.ndarray, T_q: int, T_kv: int, causal: bool) -> np.ndarray:
+def visible(rows: np.ndarray, T_q: int, T_kv: int, causal: bool, window: int = 0) -> np.ndarray:
     """Keep-mask [len(rows), T_kv]: True where query row i may see key j."""
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(T_kv, dtype=np.int64)
     if not causal:
         return np.ones((rows.size, T_kv), dtype=bool)
-    offset = T_kv - T_q
-    return j[None, :] <= (rows[:, None] + offset)
+    pos = rows[:, None] + (T_kv - T_q)  # absolute position of each query row
+    keep = j[None, :] <= pos
+    if window > 0:
+        keep &= j[None, :] > pos - window
+    return keep
 
 
 def scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
@@ -87,7 +100,7 @@ def weighted_sum(p: np.ndarray, v: np.ndarray) -> np.ndarray:
 
 
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   causal: bool, rows=None, return_p: bool = False):
+                   causal: bool, rows=None, return_p: bool = False, window: int = 0):
     """One (batch, q head) slice: q [T_q, D], k and v [T_kv, D].
 
     ``rows`` selects the query rows to compute (default: all).  Rows are
@@ -96,15 +109,18 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     """
     T_q, T_kv = q.shape[0], k.shape[0]
     rows = np.arange(T_q) if rows is None else np.asarray(rows, dtype=np.int64)
-    s = scores(q[rows], k, scale)
-    keep = visible(rows, T_q, T_kv, causal)
-    p = softmax_rows(s, keep)
-    o = weighted_sum(p, v)
+    keep = visible(rows, T_q, T_kv, causal, window)
+    seen = keep.any(axis=1)
+    p = np.zeros((rows.size, T_kv), dtype=np.float64)
+    if seen.any():
+        s = scores(q[rows[seen]], k, scale)
+        p[seen] = softmax_rows(s, keep[seen])
+    o = weighted_sum(p, v) if T_kv else np.zeros((rows.size, q.shape[1]), dtype=np.float64)
     return (o, p) if return_p else o
 
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
-              causal: bool, rows=None, heads=None, batches=None) -> np.ndarray:
+              causal: bool, rows=None, heads=None, batches=None, window: int = 0) -> np.ndarray:
     """Full forward over [B, H, T, D] tensors; returns float64 O.
 
     ``rows``/``heads``/``batches`` restrict the output to a sample (used for
@@ -124,5 +140,25 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
     for bi, b in enumerate(batches):
         for hi, h in enumerate(heads):
             g = kv_head_for(h, H_q, H_kv)
-            out[bi, hi] = attention_head(Q[b, h], K[b, g], V[b, g], scale, causal, row_sel)
+            out[bi, hi] = attention_head(Q[b, h], K[b, g], V[b, g], scale, causal, row_sel,
+                                         window=window)
+    return out
+
+
+def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, scale: float,
+                     causal: bool, window: int = 0, seqs=None) -> np.ndarray:
+    """Packed batch: q [total_q, H_q, D], k and v [total_k, H_kv, D] (token
+    major); sequence b owns query rows cu_q[b]:cu_q[b+1] and key rows
+    cu_k[b]:cu_k[b+1].  Returns float64 O [total_q, H_q, D]; rows of sequences
+    not in ``seqs`` (default: all) are left 0."""
+    total_q, H_q, D = q.shape
+    H_kv = k.shape[1]
+    out = np.zeros((total_q, H_q, D), dtype=np.float64)
+    seqs = range(len(cu_q) - 1) if seqs is None else list(seqs)
+    for b in seqs:
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        for h in range(H_q):
+            g = kv_head_for(h, H_q, H_kv)
+            out[qs:qe, h] = attention_head(q[qs:qe, h], k[ks:ke, g], v[ks:ke, g], scale, causal,
+                                           window=window)
     return out

@@ -342,6 +342,79 @@ def pin_online_merge_equals_three_pass():
         _close(got, want, 1e-12, f"online merge (causal={causal}, tiles={tiles})")
 
 
+def pin_window_one_sees_only_itself():
+    """A window of one key: each row's softmax has a single term, so the
+    output row is exactly the value row at the query's own position."""
+    r = _rng(15)
+    for T_q, T_kv in [(9, 9), (4, 11)]:
+        q, k, v = (r.standard_normal((n, 6)) for n in (T_q, T_kv, T_kv))
+        o = A.attention_head(q, k, v, 0.9, True, window=1)
+        off = T_kv - T_q
+        assert np.array_equal(o, v[np.arange(T_q) + off]), "window=1 must pick V[i + off]"
+
+
+def pin_window_equals_truncated_keys():
+    """Sliding window = plain (non-causal) attention of each row over the keys
+    inside its window, taken as a separate problem; a window covering every
+    key is plain causal attention."""
+    r = _rng(16)
+    T_q, T_kv, D, W = 10, 14, 5, 4
+    q, k, v = (r.standard_normal((n, D)) for n in (T_q, T_kv, T_kv))
+    o = A.attention_head(q, k, v, 0.6, True, window=W)
+    off = T_kv - T_q
+    for i in range(T_q):
+        p = i + off
+        lo = max(0, p - W + 1)
+        want = A.attention_head(q[i:i + 1], k[lo:p + 1], v[lo:p + 1], 0.6, False)
+        _close(o[i:i + 1], want, 1e-13, f"window row {i}")
+    _close(A.attention_head(q, k, v, 0.6, True, window=T_kv), A.attention_head(q, k, v, 0.6, True),
+           0.0, "window >= T_kv")
+
+
+def pin_chunk_is_tail_of_full_prefill():
+    """Chunked prefill: T_q queries placed at the end of T_kv keys (bottom-
+    right causal) give exactly the last T_q rows of the full causal prefill
+    whose queries are all T_kv positions."""
+    r = _rng(17)
+    T_kv, T_q, D = 12, 5, 4
+    q_full = r.standard_normal((T_kv, D))
+    k, v = r.standard_normal((T_kv, D)), r.standard_normal((T_kv, D))
+    full = A.attention_head(q_full, k, v, 0.8, True)
+    chunk = A.attention_head(q_full[-T_q:], k, v, 0.8, True)
+    _close(chunk, full[-T_q:], 1e-13, "chunk vs full prefill")
+    win_full = A.attention_head(q_full, k, v, 0.8, True, window=3)
+    win_chunk = A.attention_head(q_full[-T_q:], k, v, 0.8, True, window=3)
+    _close(win_chunk, win_full[-T_q:], 1e-13, "windowed chunk vs full")
+
+
+def pin_varlen_is_independent_sequences():
+    """A packed batch is B independent problems: with equal lengths it is the
+    dense [B][H][T][D] result transposed to token-major, and a sequence's
+    output does not depend on its neighbours."""
+    r = _rng(18)
+    B, H_q, H_kv, T, D = 3, 4, 2, 7, 5
+    Q = r.standard_normal((B, H_q, T, D))
+    K = r.standard_normal((B, H_kv, T, D))
+    V = r.standard_normal((B, H_kv, T, D))
+    dense = A.attention(Q, K, V, 0.5, True)
+    packed = lambda X: X.transpose(0, 2, 1, 3).reshape(B * T, X.shape[1], D)
+    cu = np.arange(B + 1) * T
+    got = A.attention_varlen(packed(Q), packed(K), packed(V), cu, cu, 0.5, True)
+    _close(got, packed(dense), 1e-13, "varlen vs dense")
+    # ragged: sequence 1 alone equals its slice of the packed result
+    cu_q, cu_k = np.array([0, 2, 7, 9]), np.array([0, 5, 9, 14])
+    q = r.standard_normal((9, H_q, D))
+    k = r.standard_normal((14, H_kv, D))
+    v = r.standard_normal((14, H_kv, D))
+    allo = A.attention_varlen(q, k, v, cu_q, cu_k, 0.5, True)
+    one = A.attention_varlen(q[2:7], k[5:9], v[5:9], np.array([0, 5]), np.array([0, 4]), 0.5, True)
+    _close(allo[2:7], one, 1e-13, "sequence independent of neighbours")
+    # rows before the first key (T_q > T_kv) and empty key ranges give 0
+    assert np.all(allo[2] == 0), "causal row with no visible key must be 0"
+    empty = A.attention_varlen(q[:2], k[:0], v[:0], np.array([0, 2]), np.array([0, 0]), 0.5, False)
+    assert np.all(empty == 0)
+
+
 ALL_PINS = [
     pin_rows_sum_to_one,
     pin_causal_row0_is_v0,
@@ -357,4 +430,8 @@ ALL_PINS = [
     pin_key_permutation,
     pin_linear_in_values,
     pin_online_merge_equals_three_pass,
+    pin_window_one_sees_only_itself,
+    pin_window_equals_truncated_keys,
+    pin_chunk_is_tail_of_full_prefill,
+    pin_varlen_is_independent_sequences,
 ]

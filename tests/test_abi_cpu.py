@@ -179,3 +179,53 @@ def test_paged_workspace_size():
     assert A.attn_fwd_decode_paged_workspace_bytes(2, 8, 2, 128, 12, 8, 4) == 0  # bad page size
     need = A.attn_fwd_decode_paged_workspace_bytes(2, 8, 2, 128, 16, 64, 0)
     assert need > 0 and paged(max_pages=64, ws_bytes=need - 1) == WS
+
+
+# --- sliding window and packed prefill ------------------------------------------------
+def window(q=QP, k=KP, v=VP, o=OP, B=1, H_q=4, H_kv=2, T_q=128, T_kv=128, D=64, W=16,
+           scale=0.1, dtype=BF16):
+    return A.attn_fwd_prefill_window(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, W, scale, dtype, None,
+                                     check=False)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=0), UNSUP), (dict(W=-3), UNSUP), (dict(dtype=F32), UNSUP), (dict(D=32), UNSUP),
+    (dict(T_q=129), SHAPE), (dict(H_q=3), SHAPE), (dict(scale=float("inf")), SCALE),
+    (dict(q=0), NULL), (dict(o=VP), ALIAS), (dict(k=KP + 4), ALIGN),
+])
+def test_window_rejects(kw, want):
+    assert window(**kw) == want
+
+
+def test_window_empty_ok():
+    assert window(B=0, q=0, k=0, v=0, o=0) == OK
+    assert window(T_q=0, q=0, k=0, v=0, o=0) == OK
+
+
+CQ, CK = 0x60000000, 0x70000000  # fake cu_seqlens addresses
+
+
+def varlen(q=QP, k=KP, v=VP, o=OP, cq=CQ, ck=CK, B=3, H_q=8, H_kv=2, D=128, total_q=300,
+           total_k=300, mq=200, mk=200, causal=1, W=0, scale=0.1, dtype=BF16):
+    return A.attn_fwd_prefill_varlen(q, k, v, o, cq, ck, B, H_q, H_kv, D, total_q, total_k, mq, mk,
+                                     causal, W, scale, dtype, None, check=False)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), SHAPE), (dict(H_kv=3), SHAPE), (dict(total_q=-1), SHAPE), (dict(mq=-2), SHAPE),
+    (dict(mq=1 << 20), SHAPE), (dict(mk=1 << 23), SHAPE),
+    (dict(dtype=F32), UNSUP), (dict(D=80), UNSUP), (dict(W=-1), UNSUP), (dict(W=8, causal=0), UNSUP),
+    (dict(scale=float("nan")), SCALE),
+    (dict(q=0), NULL), (dict(cq=0), NULL), (dict(ck=0), NULL),
+    (dict(v=VP + 8), ALIGN), (dict(cq=CQ + 2), ALIGN),
+    (dict(o=QP), ALIAS), (dict(o=CK - 64), ALIAS),
+])
+def test_varlen_rejects(kw, want):
+    assert varlen(**kw) == want
+
+
+def test_varlen_empty_ok():
+    assert varlen(B=0, q=0, k=0, v=0, o=0, cq=0, ck=0) == OK
+    assert varlen(mq=0, q=0, k=0, v=0, o=0, cq=0, ck=0) == OK
+    assert varlen(total_q=0, q=0, k=0, v=0, o=0, cq=0, ck=0) == OK
+    assert varlen(W=64, causal=1, cq=CQ + 4, ck=CK + 8, B=0) == OK

@@ -18,29 +18,48 @@ _orig_kv_head = A.kv_head_for
 _orig_head = A.attention_head
 
 
-def _mask_flipped(rows, T_q, T_kv, causal):
-    m = _orig_visible(rows, T_q, T_kv, causal)
+def _with_window(m, rows, T_q, T_kv, window):
+    if window <= 0:
+        return m
+    pos = np.asarray(rows)[:, None] + (T_kv - T_q)
+    return m & (np.arange(T_kv)[None, :] > pos - window)
+
+
+def _mask_flipped(rows, T_q, T_kv, causal, window=0):
+    m = _orig_visible(rows, T_q, T_kv, causal, window)
     if not causal:
         return m
     rows = np.asarray(rows)
     j = np.arange(T_kv)
-    return j[None, :] >= rows[:, None] + (T_kv - T_q)
+    return _with_window(j[None, :] >= rows[:, None] + (T_kv - T_q), rows, T_q, T_kv, window)
 
 
-def _mask_strict(rows, T_q, T_kv, causal):
+def _mask_strict(rows, T_q, T_kv, causal, window=0):
     if not causal:
-        return _orig_visible(rows, T_q, T_kv, causal)
+        return _orig_visible(rows, T_q, T_kv, causal, window)
     rows = np.asarray(rows)
     j = np.arange(T_kv)
-    return j[None, :] < rows[:, None] + (T_kv - T_q)
+    return _with_window(j[None, :] < rows[:, None] + (T_kv - T_q), rows, T_q, T_kv, window)
 
 
-def _mask_top_left(rows, T_q, T_kv, causal):
+def _mask_top_left(rows, T_q, T_kv, causal, window=0):
     if not causal:
-        return _orig_visible(rows, T_q, T_kv, causal)
+        return _orig_visible(rows, T_q, T_kv, causal, window)
     rows = np.asarray(rows)
     j = np.arange(T_kv)
-    return j[None, :] <= rows[:, None]
+    return _with_window(j[None, :] <= rows[:, None], rows, T_q, T_kv, window)
+
+
+def _window_one_too_wide(rows, T_q, T_kv, causal, window=0):
+    m = _orig_visible(rows, T_q, T_kv, causal, 0)
+    if not causal or window <= 0:
+        return m
+    pos = np.asarray(rows)[:, None] + (T_kv - T_q)
+    return m & (np.arange(T_kv)[None, :] >= pos - window)
+
+
+def _window_ignored(rows, T_q, T_kv, causal, window=0):
+    return _orig_visible(rows, T_q, T_kv, causal, 0)
 
 
 def _kv_head_tiled(h_q, H_q, H_kv):
@@ -80,8 +99,8 @@ def _scores_transposed(q_rows, k, scale):
     return s[:, ::-1].copy()
 
 
-def _head_swapped_kv(q, k, v, scale, causal, rows=None, return_p=False):
-    return _orig_head(q, v, k, scale, causal, rows, return_p)
+def _head_swapped_kv(q, k, v, scale, causal, rows=None, return_p=False, window=0):
+    return _orig_head(q, v, k, scale, causal, rows, return_p, window)
 
 
 def _weighted_sum_first_key_dropped(p, v):
@@ -94,6 +113,8 @@ MUTANTS = {
     "mask_direction_flipped": ("visible", _mask_flipped),
     "mask_excludes_diagonal": ("visible", _mask_strict),
     "causal_top_left_aligned": ("visible", _mask_top_left),
+    "window_one_key_too_wide": ("visible", _window_one_too_wide),
+    "window_ignored": ("visible", _window_ignored),
     "gqa_heads_tiled_not_grouped": ("kv_head_for", _kv_head_tiled),
     "softmax_without_max_subtraction": ("softmax_rows", _softmax_no_max),
     "softmax_not_normalised": ("softmax_rows", _softmax_unnormalised),

@@ -1,0 +1,198 @@
+"""GPU parity of the sliding-window prefill (attn_fwd_prefill_window) and the
+packed variable-length prefill (attn_fwd_prefill_varlen) against the CPU
+oracle on seeded inputs.
+
+Bar: max |O_gpu - O_oracle| <= 1.5e-2 (bf16) over every compared element, no
+write outside O, no element left unwritten.  Also bit-for-bit identities with
+the dense kernel: a window covering every key is plain causal attention, and a
+packed batch of equal lengths is the dense batch transposed."""
+import zlib
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+import oracle
+from transformer_scaled_dot_flash_amd import attn as abi
+from transformer_scaled_dot_flash_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    abi.load_library()
+
+
+def _seed(*case):
+    return zlib.crc32(repr(case).encode())
+
+
+def f64(x):
+    return inputs.as_f64(x, "bf16")
+
+
+def run_window(q, k, v, window, scale):
+    torch = G.torch_mod()
+    B, H_q, T_q, D = q.shape
+    _, H_kv, T_kv, _ = k.shape
+    qd, kd, vd = (G.to_device(x, "bf16") for x in (q, k, v))
+    buf, o = G.guarded_output((B, H_q, T_q, D), "bf16")
+    G.note(f"attn_fwd_prefill_window B={B} H_q={H_q} H_kv={H_kv} T_q={T_q} T_kv={T_kv} D={D} W={window}")
+    abi.attn_fwd_prefill_window(qd, kd, vd, o, B, H_q, H_kv, T_q, T_kv, D, window, scale,
+                                abi.ATTN_BF16, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    G.check_guards(buf, "bf16", "window prefill")
+    return G.to_f64(o, "bf16")
+
+
+def run_varlen(q, k, v, cu_q, cu_k, causal, window, scale):
+    torch = G.torch_mod()
+    total_q, H_q, D = q.shape
+    total_k, H_kv, _ = k.shape
+    B = len(cu_q) - 1
+    lq, lk = np.diff(cu_q), np.diff(cu_k)
+    qd, kd, vd = (G.to_device(x, "bf16") for x in (q, k, v))
+    cq = torch.from_numpy(np.asarray(cu_q, np.int32)).cuda()
+    ck = torch.from_numpy(np.asarray(cu_k, np.int32)).cuda()
+    buf, o = G.guarded_output((total_q, H_q, D), "bf16")
+    G.note(f"attn_fwd_prefill_varlen B={B} H_q={H_q} H_kv={H_kv} D={D} lens_q={list(lq)[:6]} "
+           f"lens_k={list(lk)[:6]} causal={int(causal)} W={window}")
+    abi.attn_fwd_prefill_varlen(qd, kd, vd, o, cq, ck, B, H_q, H_kv, D, total_q, total_k,
+                                int(lq.max(initial=0)), int(lk.max(initial=0)), causal, window, scale,
+                                abi.ATTN_BF16, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    G.check_guards(buf, "bf16", "varlen prefill")
+    return G.to_f64(o, "bf16")
+
+
+# --- sliding window ---------------------------------------------------------------
+WINDOW_CASES = [
+    # B, H_q, H_kv, T_q, T_kv, D, window
+    (1, 4, 2, 300, 300, 128, 64),
+    (2, 8, 2, 1000, 1000, 64, 100),
+    (1, 2, 1, 257, 513, 128, 33),     # chunk of queries at the end of the keys
+    (1, 4, 4, 129, 129, 64, 1),       # each row sees only itself
+    (1, 4, 1, 700, 700, 128, 255),
+    (1, 8, 8, 2048, 2048, 128, 1000),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "B{}H{}/{}T{}x{}D{}W{}".format(*c))
+def test_window_matches_oracle(case):
+    B, H_q, H_kv, T_q, T_kv, D, W = case
+    s = _seed("win", case)
+    q = inputs.normal(s + 1, (B, H_q, T_q, D), "bf16")
+    k = inputs.normal(s + 2, (B, H_kv, T_kv, D), "bf16")
+    v = inputs.normal(s + 3, (B, H_kv, T_kv, D), "bf16")
+    scale = 1.0 / np.sqrt(D)
+    got = run_window(q, k, v, W, scale)
+    rows = None if T_q <= 1000 else sorted(set(np.random.default_rng(s).integers(0, T_q, 64).tolist())
+                                           | {0, 1, W - 1, W, W + 1, T_q - 1})
+    want = oracle.attention(f64(q), f64(k), f64(v), scale, True, rows=rows, window=W)
+    if rows is not None:
+        got = got[:, :, rows]
+    err = G.max_err(got, want)
+    print(f"window {case}: max|dO| = {err:.3e}")
+    assert err <= G.TOL["bf16"]
+
+
+def test_window_large_problem_sampled():
+    # 8-wave launch shape (many workgroups), first tiles skipped for late rows
+    B, H_q, H_kv, T, D, W = 1, 32, 8, 4096, 128, 1024
+    s = _seed("winbig")
+    q = inputs.normal(s + 1, (B, H_q, T, D), "bf16")
+    k = inputs.normal(s + 2, (B, H_kv, T, D), "bf16")
+    v = inputs.normal(s + 3, (B, H_kv, T, D), "bf16")
+    got = run_window(q, k, v, W, 1.0 / np.sqrt(D))
+    rows = [0, 255, 256, 1023, 1024, 1025, 2047, 2048, 3000, 4095]
+    heads = [0, 5, 17, 31]
+    want = oracle.attention(f64(q), f64(k), f64(v), 1.0 / np.sqrt(D), True, rows=rows, heads=heads,
+                            window=W)
+    err = G.max_err(got[:, heads][:, :, rows], want)
+    assert err <= G.TOL["bf16"], err
+
+
+@pytest.mark.parametrize("T_q,T_kv,D", [(300, 300, 128), (100, 260, 64), (2048, 2048, 128)])
+def test_full_window_is_plain_causal_bitwise(T_q, T_kv, D):
+    s = _seed("winfull", T_q, T_kv, D)
+    q = inputs.normal(s + 1, (1, 4, T_q, D), "bf16")
+    k = inputs.normal(s + 2, (1, 2, T_kv, D), "bf16")
+    v = inputs.normal(s + 3, (1, 2, T_kv, D), "bf16")
+    a = run_window(q, k, v, T_kv + 5, 0.1)
+    b = G.prefill(q, k, v, True, 0.1, "bf16")
+    assert np.array_equal(a, b)
+
+
+# --- packed variable-length batches ---------------------------------------------------
+def make_varlen(lens_q, lens_k, H_q, H_kv, D, tag):
+    s = _seed("varlen", tuple(lens_q), tuple(lens_k), H_q, H_kv, D, tag)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int64)
+    q = inputs.normal(s + 1, (int(cu_q[-1]), H_q, D), "bf16")
+    k = inputs.normal(s + 2, (int(cu_k[-1]), H_kv, D), "bf16")
+    v = inputs.normal(s + 3, (int(cu_k[-1]), H_kv, D), "bf16")
+    return q, k, v, cu_q, cu_k
+
+
+VARLEN_CASES = [
+    # lens_q, lens_k, H_q, H_kv, D, causal, window
+    ([100, 1, 257, 64], [100, 1, 257, 64], 4, 2, 128, True, 0),
+    ([100, 1, 257, 64], [100, 1, 257, 64], 4, 2, 64, False, 0),
+    ([64, 200, 5], [200, 200, 300], 8, 2, 128, True, 0),      # chunks at the end of the keys
+    ([300, 10], [150, 10], 4, 4, 64, True, 0),                # rows before the first key -> 0
+    ([0, 33, 0, 129], [0, 33, 17, 129], 4, 1, 128, True, 0),  # empty sequences / key ranges
+    ([500, 300, 700], [500, 300, 700], 8, 2, 128, True, 128), # sliding window per sequence
+    ([129, 1000], [129, 1000], 2, 2, 64, True, 1),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: f"q{c[0]}k{c[1]}H{c[2]}/{c[3]}D{c[4]}c{int(c[5])}W{c[6]}")
+def test_varlen_matches_oracle(case):
+    lens_q, lens_k, H_q, H_kv, D, causal, window = case
+    q, k, v, cu_q, cu_k = make_varlen(lens_q, lens_k, H_q, H_kv, D, "p")
+    scale = 1.0 / np.sqrt(D)
+    got = run_varlen(q, k, v, cu_q, cu_k, causal, window, scale)
+    want = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_q, cu_k, scale, causal, window)
+    err = G.max_err(got, want)
+    print(f"varlen {case}: max|dO| = {err:.3e}")
+    assert err <= G.TOL["bf16"]
+    # rows that see no key are exactly 0
+    for b in range(len(lens_q)):
+        if lens_k[b] == 0 or (causal and lens_q[b] > lens_k[b]):
+            n0 = lens_q[b] if lens_k[b] == 0 else lens_q[b] - lens_k[b]
+            assert np.all(got[cu_q[b]:cu_q[b] + n0] == 0)
+
+
+def test_varlen_large_mixed_batch_sampled():
+    lens = [4096, 1000, 3000, 2048, 77]
+    H_q, H_kv, D = 32, 8, 128
+    q, k, v, cu_q, cu_k = make_varlen(lens, lens, H_q, H_kv, D, "big")
+    got = run_varlen(q, k, v, cu_q, cu_k, True, 0, 1.0 / np.sqrt(D))
+    rng = np.random.default_rng(3)
+    for b in range(len(lens)):
+        rows = sorted(set(rng.integers(0, lens[b], 12).tolist()) | {0, lens[b] - 1})
+        qs, ks = int(cu_q[b]), int(cu_k[b])
+        for h in (0, 13, 31):
+            g = h // (H_q // H_kv)
+            want = oracle.attention_head(f64(q[qs:qs + lens[b], h]), f64(k[ks:ks + lens[b], g]),
+                                         f64(v[ks:ks + lens[b], g]), 1.0 / np.sqrt(D), True, rows=rows)
+            err = G.max_err(got[qs + np.asarray(rows), h], want)
+            assert err <= G.TOL["bf16"], (b, h, err)
+
+
+@pytest.mark.parametrize("T,D,causal", [(513, 128, True), (300, 64, False), (4096, 128, True)])
+def test_varlen_equal_lengths_is_dense_bitwise(T, D, causal):
+    B, H_q, H_kv = 2, 8, 2
+    s = _seed("vdense", T, D, causal)
+    q = inputs.normal(s + 1, (B, H_q, T, D), "bf16")
+    k = inputs.normal(s + 2, (B, H_kv, T, D), "bf16")
+    v = inputs.normal(s + 3, (B, H_kv, T, D), "bf16")
+    dense = G.prefill(q, k, v, causal, 0.09, "bf16")
+    packed = lambda X: np.ascontiguousarray(X.transpose(0, 2, 1, 3).reshape(B * T, X.shape[1], D))
+    cu = np.arange(B + 1) * T
+    got = run_varlen(packed(q), packed(k), packed(v), cu, cu, causal, 0, 0.09)
+    assert np.array_equal(got, dense.transpose(0, 2, 1, 3).reshape(B * T, H_q, D))

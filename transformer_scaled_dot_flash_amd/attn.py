@@ -33,6 +33,8 @@ STATUS_NAMES = {
 
 EXPORTED = (
     "attn_fwd_prefill",
+    "attn_fwd_prefill_window",
+    "attn_fwd_prefill_varlen",
     "attn_fwd_decode",
     "attn_fwd_decode_workspace_bytes",
     "attn_fwd_decode_default_splits",
@@ -72,6 +74,11 @@ def load_library(path: Path | str | None = None):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
     lib.attn_fwd_prefill.restype = i
+    lib.attn_fwd_prefill_window.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd_prefill_window.restype = i
+    lib.attn_fwd_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f,
+                                            i, vp]
+    lib.attn_fwd_prefill_varlen.restype = i
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.attn_fwd_decode.restype = i
     lib.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -122,6 +129,29 @@ def attn_fwd_prefill(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, causal, scale, dtyp
                               1 if causal else 0, float(scale), dtype, _stream(stream))
     if check:
         _check(st, "attn_fwd_prefill")
+    return st
+
+
+def attn_fwd_prefill_window(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, window, scale, dtype,
+                            stream=None, check=True) -> int:
+    lib = load_library()
+    st = lib.attn_fwd_prefill_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H_q, H_kv, T_q, T_kv, D,
+                                     window, float(scale), dtype, _stream(stream))
+    if check:
+        _check(st, "attn_fwd_prefill_window")
+    return st
+
+
+def attn_fwd_prefill_varlen(q, k, v, o, cu_seqlens_q, cu_seqlens_k, B, H_q, H_kv, D, total_q,
+                            total_k, max_seqlen_q, max_seqlen_k, causal, window, scale, dtype,
+                            stream=None, check=True) -> int:
+    lib = load_library()
+    st = lib.attn_fwd_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens_q),
+                                     _ptr(cu_seqlens_k), B, H_q, H_kv, D, total_q, total_k,
+                                     max_seqlen_q, max_seqlen_k, 1 if causal else 0, window,
+                                     float(scale), dtype, _stream(stream))
+    if check:
+        _check(st, "attn_fwd_prefill_varlen")
     return st
 
 

@@ -174,6 +174,90 @@ attn_status_t attn_fwd_prefill(const void* q, const void* k, const void* v, void
                                          : attn::launch_prefill_f32(a, s));
 }
 
+attn_status_t attn_fwd_prefill_window(const void* q, const void* k, const void* v, void* o, int B,
+                                      int H_q, int H_kv, int T_q, int T_kv, int D, int window,
+                                      float scale, int dtype, void* stream) {
+    attn_status_t st = check_params(B, H_q, H_kv, T_q, T_kv, D, dtype, scale);
+    if (st != ATTN_OK) return st;
+    if (T_q > T_kv) return ATTN_ERR_INVALID_SHAPE;
+    if (dtype != ATTN_BF16 || window < 1) return ATTN_ERR_UNSUPPORTED;
+    const long long g_bf16 = (long long)B * H_q * ((T_q + 127) / 128);
+    if (g_bf16 > 0x7fffffffLL) return ATTN_ERR_INVALID_SHAPE;
+    if (B == 0 || T_q == 0) return ATTN_OK;
+    st = check_tensors(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, dtype);
+    if (st != ATTN_OK) return st;
+
+    attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.T_q = T_q;
+    a.T_kv = T_kv;
+    a.D = D;
+    a.causal = 1;
+    a.scale = scale;
+    a.scale_log2 = log2_scale(scale);
+    positive_scale(scale, &a.c_log2, &a.neg_q);
+    a.window = window >= T_kv ? 0 : window;  // a window covering every key is plain causal
+    return hip_status(attn::launch_prefill_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+attn_status_t attn_fwd_prefill_varlen(const void* q, const void* k, const void* v, void* o,
+                                      const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                                      int H_q, int H_kv, int D, int total_q, int total_k,
+                                      int max_seqlen_q, int max_seqlen_k, int causal, int window,
+                                      float scale, int dtype, void* stream) {
+    if (B < 0 || H_q <= 0 || H_kv <= 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 ||
+        max_seqlen_k < 0)
+        return ATTN_ERR_INVALID_SHAPE;
+    if (H_q % H_kv != 0) return ATTN_ERR_INVALID_SHAPE;
+    if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_SCALE;
+    // Rows of one sequence are addressed with 32-bit byte offsets (with
+    // margin for the last partial tile); the grid covers max_seqlen_q rows.
+    if ((long long)(max_seqlen_q + 256) * H_q * D * 2 >= (1LL << 31) ||
+        (long long)(max_seqlen_k + 64) * H_kv * D * 2 >= (1LL << 31))
+        return ATTN_ERR_INVALID_SHAPE;
+    if ((long long)B * H_q * ((max_seqlen_q + 127) / 128) > 0x7fffffffLL) return ATTN_ERR_INVALID_SHAPE;
+    if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
+    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL_PTR;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+        (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+        return ATTN_ERR_ALIGNMENT;
+    const size_t nq = (size_t)total_q * H_q * D * 2;
+    const size_t nkv = (size_t)total_k * H_kv * D * 2;
+    const size_t ncu = (size_t)(B + 1) * 4;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv) ||
+        overlaps(o, nq, cu_seqlens_q, ncu) || overlaps(o, nq, cu_seqlens_k, ncu))
+        return ATTN_ERR_ALIAS;
+
+    attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.T_q = max_seqlen_q;   // sizes the grid; each workgroup reads its sequence's lengths
+    a.T_kv = max_seqlen_k;
+    a.D = D;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    a.scale_log2 = log2_scale(scale);
+    positive_scale(scale, &a.c_log2, &a.neg_q);
+    a.window = window;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    return hip_status(attn::launch_prefill_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void* o, int B,
                               int H_q, int H_kv, int T_q, int T_kv, int D, int causal,
                               float scale, int dtype, int num_splits, void* workspace,

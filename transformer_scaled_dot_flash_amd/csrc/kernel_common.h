@@ -200,6 +200,9 @@ struct PrefillArgs {
     float scale_log2;  // scale * log2(e), rounded to float
     float c_log2;      // |scale| * log2(e), >= FLT_MIN (0 becomes FLT_MIN: same weights)
     int neg_q;         // 1 when scale < 0: the kernels flip Q's sign instead
+    int window;        // causal sliding window in keys (0: none)
+    const int* cu_q;   // packed batch: [B + 1] row offsets of each sequence's
+    const int* cu_k;   //   queries / keys (nullptr: contiguous [B][H][T][D])
 };
 
 // Paged KV cache of the decode kernel (block_table == nullptr: contiguous).

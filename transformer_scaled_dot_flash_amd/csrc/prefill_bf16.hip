@@ -125,11 +125,12 @@ __device__ inline void score_tile(STile<BN, RB>& st, const unsigned char* kst,
     }
 }
 
-template <int D, bool CAUSAL, int RB, int BN, int WAVES, int WPE>
+template <int D, bool CAUSAL, bool VARLEN, int RB, int BN, int WAVES, int WPE>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
 prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                     const bf16* __restrict__ V, bf16* __restrict__ O, int B, int H_q, int H_kv,
-                    int T_q, int T_kv, int n_qt, float c, int neg_q) {
+                    int T_q, int T_kv, int n_qt, float c, int neg_q, int window,
+                    const int* __restrict__ cu_q, const int* __restrict__ cu_k) {
     constexpr int WROWS = 32 * RB;                // query rows per wave
     constexpr int BM = WROWS * WAVES;             // query rows per workgroup
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
@@ -149,29 +150,55 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int hi = lane >> 5;
 
     const TileCoord tc = map_tile(blockIdx.x, B, H_q, H_kv, n_qt, CAUSAL);
-    const uint32_t q_bytes = (uint32_t)T_q * ROWB;
-    const uint32_t kv_bytes = (uint32_t)T_kv * ROWB;
-    const auto rQ = make_rsrc(Q + (size_t)(tc.b * H_q + tc.hq) * T_q * D, q_bytes);
-    const auto rK = make_rsrc(K + (size_t)(tc.b * H_kv + tc.hk) * T_kv * D, kv_bytes);
-    const auto rV = make_rsrc(V + (size_t)(tc.b * H_kv + tc.hk) * T_kv * D, kv_bytes);
-    const auto rO = make_rsrc(O + (size_t)(tc.b * H_q + tc.hq) * T_q * D, q_bytes);
+
+    // Rows of this (sequence, head): contiguous [B][H][T][D] (row stride D),
+    // or packed token-major [total][H][D] with the sequence's rows starting at
+    // cu[b] (row stride H * D).
+    const int SQ = VARLEN ? H_q * D : D;   // row strides in elements
+    const int SK = VARLEN ? H_kv * D : D;
+    size_t q_base, kv_base;
+    if constexpr (VARLEN) {
+        const int qs = cu_q[tc.b], ks = cu_k[tc.b];
+        T_q = max(cu_q[tc.b + 1] - qs, 0);
+        T_kv = max(cu_k[tc.b + 1] - ks, 0);
+        q_base = (size_t)qs * SQ + (size_t)tc.hq * D;
+        kv_base = (size_t)ks * SK + (size_t)tc.hk * D;
+    } else {
+        q_base = (size_t)(tc.b * H_q + tc.hq) * T_q * D;
+        kv_base = (size_t)(tc.b * H_kv + tc.hk) * T_kv * D;
+    }
+    const int q0 = tc.qt * BM;
+    if (q0 >= T_q) return;  // a short sequence of a packed batch: no rows here
+    const uint32_t q_bytes = (uint32_t)((T_q - 1) * SQ + D) * 2;
+    const uint32_t kv_bytes = T_kv > 0 ? (uint32_t)((T_kv - 1) * SK + D) * 2 : 0u;
+    const auto rQ = make_rsrc(Q + q_base, q_bytes);
+    const auto rK = make_rsrc(K + kv_base, kv_bytes);
+    const auto rV = make_rsrc(V + kv_base, kv_bytes);
+    const auto rO = make_rsrc(O + q_base, q_bytes);
 
     const int off = T_kv - T_q;  // bottom-right causal alignment
-    const int q0 = tc.qt * BM;
     const int row0 = q0 + wave * WROWS;  // first row of this wave
+    // Sliding window (causal only): row i sees keys i + off - window + 1 ..
+    // i + off.
+    const bool windowed = CAUSAL && window > 0;
+    auto first_key = [&](int row) { return windowed ? max(0, row + off - window + 1) : 0; };
 
     // Key ranges: the workgroup's, this wave's, each row block's.
     const int last_row = min(T_q, q0 + BM) - 1;
-    const int kv_end = CAUSAL ? min(T_kv, last_row + off + 1) : T_kv;
+    const int kv_end = CAUSAL ? max(0, min(T_kv, last_row + off + 1)) : T_kv;
     const int n_kt = (kv_end + BN - 1) / BN;
-    int rb_kv_end[RB];
+    const int t_lo = min(first_key(q0) / BN, n_kt);  // tiles left of every row's window are never visited
+    int rb_kv_end[RB], rb_kv_begin[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int r0 = row0 + rb * 32;
         const int rlast = min(T_q - 1, r0 + 31);
-        rb_kv_end[rb] = (r0 >= T_q) ? 0 : (CAUSAL ? min(T_kv, rlast + off + 1) : T_kv);
+        rb_kv_end[rb] = (r0 >= T_q) ? 0 : (CAUSAL ? max(0, min(T_kv, rlast + off + 1)) : T_kv);
+        rb_kv_begin[rb] = first_key(r0);
     }
     const int wave_kv_end = rb_kv_end[RB - 1];  // the last row block sees the most keys
+    const int wave_kv_begin = rb_kv_begin[0];   // the first row block starts leftmost
+    auto wave_live = [&](int j0) { return j0 < wave_kv_end && j0 + BN > wave_kv_begin; };
 
     // Q fragments: B operands of S^T = K Q^T (column = query row, 8 features).
     // Rows past T_q read as zero.  A negative scale is folded into Q's sign
@@ -181,14 +208,14 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            u32x4 w = buf_load_b128(rQ, (uint32_t)((row0 + rb * 32 + l32) * D + 16 * s + 8 * hi) * 2);
+            u32x4 w = buf_load_b128(rQ, (uint32_t)((row0 + rb * 32 + l32) * SQ + 16 * s + 8 * hi) * 2);
             if (neg_q) w ^= 0x80008000u;
             qf[rb][s] = __builtin_bit_cast(bf16x8, w);
         }
     }
 
     // Direct-to-LDS loads of one K or V tile.  Keys past T_kv are outside
-    // the buffer range and load as zero.
+    // the buffer range and load as zero.  Tile t uses ring slot (t - t_lo) & 1.
     auto issue = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int t) {
         const int j0 = t * BN;
 #pragma unroll
@@ -197,19 +224,20 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             const int p = blk * 64 + lane;  // chunk slot in the tile
             const int row = p / CPR;
             const int logical = (p % CPR) ^ swz<CPR>(row);
-            buf_load_lds16(r, dst + blk * 1024, (uint32_t)(j0 + row) * ROWB + logical * 16);
+            buf_load_lds16(r, dst + blk * 1024, (uint32_t)(j0 + row) * SK * 2 + logical * 16);
         }
     };
-    auto issue_k = [&](int t) { issue(rK, kring + (t & 1) * TILE, t); };
-    auto issue_v = [&](int t) { issue(rV, vring + (t & 1) * TILE, t); };
+    auto issue_k = [&](int t) { issue(rK, kring + ((t - t_lo) & 1) * TILE, t); };
+    auto issue_v = [&](int t) { issue(rV, vring + ((t - t_lo) & 1) * TILE, t); };
 
-    // Prologue: K(0), V(0), K(1).  Step t then issues K(t+2) into K(t)'s slot
-    // and V(t+1) into V(t-1)'s slot, both read for the last time in step t-1.
-    if (n_kt > 0) {
-        issue_k(0);
-        issue_v(0);
+    // Prologue: K(t_lo), V(t_lo), K(t_lo+1).  Step t then issues K(t+2) into
+    // K(t)'s slot and V(t+1) into V(t-1)'s slot, both read for the last time
+    // in step t-1.
+    if (t_lo < n_kt) {
+        issue_k(t_lo);
+        issue_v(t_lo);
     }
-    if (n_kt > 1) issue_k(1);
+    if (t_lo + 1 < n_kt) issue_k(t_lo + 1);
 
     f32x16 oacc[RB][D / 32];
     float m_use[RB];  // base of the exponent (log2 units), per row
@@ -228,15 +256,15 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     pv_lane_offsets<D>(voff, lane);
 
     STile<BN, RB> s_a, s_b;  // scores of the current and the next tile, alternating
-    if (n_kt > 0) {
+    if (t_lo < n_kt) {
         wait_vmem_all();
         __syncthreads();
-        if (0 < wave_kv_end) score_tile<D, BN, RB>(s_a, kring, qf, l32, hi);
+        if (wave_live(t_lo * BN)) score_tile<D, BN, RB>(s_a, kring, qf, l32, hi);
     }
 
-    // Step t with PAR = t & 1 known at compile time: K(t+1) sits in slot
-    // 1 - PAR, V(t) in slot PAR.  s_cur holds the scores of tile t, s_next
-    // receives those of tile t+1.
+    // Step t with PAR = (t - t_lo) & 1 known at compile time: K(t+1) sits in
+    // slot 1 - PAR, V(t) in slot PAR.  s_cur holds the scores of tile t,
+    // s_next receives those of tile t+1.
     auto step = [&](int t, auto par, STile<BN, RB>& s_cur, STile<BN, RB>& s_next) {
         constexpr int PAR = decltype(par)::value;
         const int j0 = t * BN;
@@ -248,21 +276,31 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         if (t + 2 < n_kt) issue_k(t + 2);
         if (t + 1 < n_kt) issue_v(t + 1);
         if (j0 >= wave_kv_end) return;  // this and all later tiles are above the diagonal
+        if (j0 + BN <= wave_kv_begin) {
+            // Left of this wave's window.  If the next tile is its first, its
+            // scores are needed in the next step.
+            if (wave_live(j0 + BN)) score_tile<D, BN, RB>(s_next, kring + (1 - PAR) * TILE, qf, l32, hi);
+            return;
+        }
 
         // Per row block: mask, base update.
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            if (j0 >= rb_kv_end[rb]) continue;  // this block's rows see none of these keys
+            // This block's rows see none of these keys: skip.
+            if (j0 >= rb_kv_end[rb] || j0 + BN <= rb_kv_begin[rb]) continue;
             const int r0 = row0 + rb * 32;
-            const bool need_mask = (j0 + BN > T_kv) || (CAUSAL && j0 + BN - 1 > r0 + off);
+            const int rlast = min(T_q - 1, r0 + 31);
+            const bool need_mask = (j0 + BN > T_kv) || (CAUSAL && j0 + BN - 1 > r0 + off) ||
+                                   (windowed && j0 < first_key(rlast));
             if (need_mask) {
                 const int lim = CAUSAL ? min(T_kv - 1, r0 + l32 + off) : T_kv - 1;
+                const int lo = windowed ? r0 + l32 + off - window + 1 : 0;
 #pragma unroll
                 for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int key = j0 + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-                        s_cur.acc[rb][kb][j] = key <= lim ? s_cur.acc[rb][kb][j] : -INFINITY;
+                        s_cur.acc[rb][kb][j] = (key <= lim && key >= lo) ? s_cur.acc[rb][kb][j] : -INFINITY;
                     }
                 }
             }
@@ -303,7 +341,7 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         for (int rb = 0; rb < RB; ++rb) {
             // A row block with no visible key in this tile contributes
             // nothing: its weights are zero.
-            const bool live = j0 < rb_kv_end[rb];
+            const bool live = j0 < rb_kv_end[rb] && j0 + BN > rb_kv_begin[rb];
             const float m_sub = (m_use[rb] == -INFINITY) ? 0.f : m_use[rb];
             const float cc = live ? c : 0.f;
             const float msub = live ? m_sub : INFINITY;
@@ -334,17 +372,18 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         }
         pv_tile<D, BN / 16, RB>(oacc, pb, va);
     };
-    for (int t = 0; t < n_kt; t += 2) {
+    for (int t = t_lo; t < n_kt; t += 2) {
         step(t, std::integral_constant<int, 0>{}, s_a, s_b);
         if (t + 1 < n_kt) step(t + 1, std::integral_constant<int, 1>{}, s_b, s_a);
     }
 
     // Epilogue: O = O_acc / l, rounded once to bf16.  Rows past T_q fall
-    // outside the buffer range and their stores are dropped.
+    // outside the buffer range and their stores are dropped.  A row that
+    // sees no key (possible only in a packed batch) gets O = 0.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l_tot = l_run[rb] + swap_halves(l_run[rb], xaddr);
-        const float inv = 1.f / l_tot;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const int my_row = row0 + rb * 32 + l32;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -354,22 +393,22 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
                 for (int r = 0; r < 4; ++r) w[r] = (bf16)(oacc[rb][db][4 * g4 + r] * inv);
                 buf_store_b64(__builtin_bit_cast(u32x2, w), rO,
-                              (uint32_t)(my_row * D + db * 32 + 8 * g4 + 4 * hi) * 2);
+                              (uint32_t)(my_row * SQ + db * 32 + 8 * g4 + 4 * hi) * 2);
             }
         }
     }
 }
 
-template <int D, bool CAUSAL, int RB, int BN, int WAVES, int WPE>
+template <int D, bool CAUSAL, bool VARLEN, int RB, int BN, int WAVES, int WPE>
 hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
     constexpr int BM = 32 * RB * WAVES;
     const int n_qt = (a.T_q + BM - 1) / BM;
     const long long grid = (long long)a.B * a.H_q * n_qt;
-    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, RB, BN, WAVES, WPE>, dim3((unsigned)grid),
-                         dim3(64 * WAVES), 0, s, static_cast<const bf16*>(a.q),
+    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, VARLEN, RB, BN, WAVES, WPE>,
+                         dim3((unsigned)grid), dim3(64 * WAVES), 0, s, static_cast<const bf16*>(a.q),
                          static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                          static_cast<bf16*>(a.o), a.B, a.H_q, a.H_kv, a.T_q, a.T_kv, n_qt, a.c_log2,
-                         a.neg_q);
+                         a.neg_q, a.window, a.cu_q, a.cu_k);
 }
 
 #ifndef PF_FORCE
@@ -379,19 +418,24 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
 // Large problems (at least two 256-row workgroups per CU): 8 waves, one
 // workgroup per CU.  Otherwise 4 waves, two workgroups per CU.  Both use
 // 64 KiB of LDS (two K and two V tiles).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
     const long long wg_big = (long long)a.B * a.H_q * ((a.T_q + 255) / 256);
     const bool big = PF_FORCE == 2 || (PF_FORCE == 0 && wg_big >= 512);
-    if (big) return launch_cfg<D, CAUSAL, 1, 64, 8, 2>(a, s);
-    return launch_cfg<D, CAUSAL, 1, 64, 4, 2>(a, s);
+    if (big) return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 8, 2>(a, s);
+    return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 4, 2>(a, s);
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
+    if (a.cu_q) return a.causal ? launch_one<D, true, true>(a, s) : launch_one<D, false, true>(a, s);
+    return a.causal ? launch_one<D, true, false>(a, s) : launch_one<D, false, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-    if (a.D == 128) return a.causal ? launch_one<128, true>(a, s) : launch_one<128, false>(a, s);
-    return a.causal ? launch_one<64, true>(a, s) : launch_one<64, false>(a, s);
+    return a.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
 
 }  // namespace attn
