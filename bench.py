@@ -180,6 +180,91 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
 
 
 PAGE_SIZE = 16
+WINDOW = 4096                 # sliding-window line: Mistral-style 4K window
+VARLEN_TOKENS = 32768         # packed-batch line: total query tokens
+
+
+def time_calls(torch, stream, run, warmup, settle, steps):
+    """Average and minimum duration (ms) of ``run`` over ``steps`` calls, each
+    bracketed by events on ``stream``, after warm-up."""
+    t_settle = time.perf_counter() + settle
+    done = 0
+    while done < warmup or time.perf_counter() < t_settle:
+        run()
+        done += 1
+        if done % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return sum(ms) / steps, min(ms)
+
+
+def mfma_line(metric, workload, flops, avg, mn, kernel):
+    tf = flops / (avg * 1e-3) / 1e12
+    return {"metric": metric, "value": round(tf, 1), "unit": "TFLOP/s",
+            "config": {"workload": workload, "flops": flops},
+            "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "avg_launch_us": round(avg * 1e3, 2), "min_launch_us": round(mn * 1e3, 2)}}
+
+
+def window_prefill_line(abi, torch, wp, qp, kp, vp, stream, warmup, settle, steps):
+    """Causal sliding window W=4096 on the T=8192 GQA prefill inputs."""
+    op = torch.empty_like(qp)
+    T, W = wp.T_q, WINDOW
+    pairs = sum(min(i + 1, W) for i in range(T))
+    flops = 4 * wp.B * wp.H_q * wp.D * pairs
+
+    def run():
+        abi.attn_fwd_prefill_window(qp, kp, vp, op, wp.B, wp.H_q, wp.H_kv, T, wp.T_kv, wp.D, W,
+                                    wp.scale, abi.ATTN_BF16, stream)
+    log("window prefill")
+    avg, mn = time_calls(torch, stream, run, warmup, settle, steps)
+    return mfma_line("sliding-window prefill TFLOP/s",
+                     f"causal GQA B=1 H_q=32 H_kv=8 T=8192 D=128 bf16, window {W}", flops, avg, mn,
+                     "prefill_bf16_kernel<128,64,causal> (window)")
+
+
+def varlen_prefill_line(abi, torch, np, stream, dev, warmup, settle, steps):
+    """Packed causal GQA batch of mixed lengths (H_q=32, H_kv=8, D=128, bf16):
+    lengths drawn once from a seeded uniform on [128, 4096], 32K tokens."""
+    from transformer_scaled_dot_flash_amd import inputs
+    rng = np.random.default_rng(2024)
+    lens = []
+    while sum(lens) < VARLEN_TOKENS:
+        lens.append(int(rng.integers(128, 4097)))
+    lens[-1] -= sum(lens) - VARLEN_TOKENS
+    lens = [x for x in lens if x > 0]
+    H_q, H_kv, D = 32, 8, 128
+    total = sum(lens)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
+
+    def mk(seed, h):
+        bits = inputs.normal(seed, (total, h, D), "bf16")
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = mk(7001, H_q), mk(7002, H_kv), mk(7003, H_kv)
+    o = torch.empty_like(q)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    flops = sum(4 * H_q * D * t * (t + 1) // 2 for t in lens)
+
+    def run():
+        abi.attn_fwd_prefill_varlen(q, k, v, o, cu, cu, len(lens), H_q, H_kv, D, total, total,
+                                    max(lens), max(lens), True, 0, scale, abi.ATTN_BF16, stream)
+    log(f"varlen prefill ({len(lens)} sequences)")
+    avg, mn = time_calls(torch, stream, run, warmup, settle, steps)
+    line = mfma_line("packed variable-length prefill TFLOP/s",
+                     f"{len(lens)} causal GQA sequences, lengths U[128, 4096] (seed 2024), "
+                     f"{total} tokens, H_q=32 H_kv=8 D=128 bf16", flops, avg, mn,
+                     "prefill_bf16_kernel<128,64,causal,packed>")
+    line["config"]["lengths"] = lens
+    return line
 
 
 def time_paged_decode(abi, torch, wd, kd, vd, qd, od_contig, stream, dev, warmup, settle, steps):
@@ -261,6 +346,8 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "paged"], default=None,
                     help="time one part only (for profiling runs)")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV decode line")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the sliding-window and packed-batch prefill lines")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -348,6 +435,12 @@ def main():
     p_tflops = wp.flops() / (p_avg * 1e-3) / 1e12 if do_p else None
     d_gbs = wd.bytes() / (d_avg * 1e-3) / 1e9 if do_d else None
 
+    extra = {}
+    if args.only is None and not args.no_extra:
+        extra["window_prefill"] = window_prefill_line(abi, torch, wp, qp, kp, vp, stream, args.warmup,
+                                                      args.settle, min(K, 20))
+        extra["varlen_prefill"] = varlen_prefill_line(abi, torch, np, stream, dev, args.warmup,
+                                                      args.settle, min(K, 20))
     paged = None
     if do_pg:
         paged = time_paged_decode(abi, torch, wd, kd, vd, qd, od if do_d else None, stream, dev,
@@ -419,6 +512,7 @@ def main():
         }
     if paged is not None:
         result["paged_decode"] = paged
+    result.update(extra)
     if not args.no_cpu_baseline and do_p:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline()

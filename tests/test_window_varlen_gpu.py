@@ -196,3 +196,19 @@ def test_varlen_equal_lengths_is_dense_bitwise(T, D, causal):
     cu = np.arange(B + 1) * T
     got = run_varlen(packed(q), packed(k), packed(v), cu, cu, causal, 0, 0.09)
     assert np.array_equal(got, dense.transpose(0, 2, 1, 3).reshape(B * T, H_q, D))
+
+
+def test_varlen_long_sequences_eight_wave_shape_sampled():
+    # average length >= 4096 and >= 512 workgroups of 256 rows: the 8-wave launch
+    lens_q, lens_k = [4100, 4500], [4100, 4700]
+    H_q, H_kv, D = 32, 8, 128
+    q, k, v, cu_q, cu_k = make_varlen(lens_q, lens_k, H_q, H_kv, D, "long")
+    got = run_varlen(q, k, v, cu_q, cu_k, True, 0, 1.0 / np.sqrt(D))
+    for b in range(2):
+        rows = [0, 1, 255, 256, 2047, lens_q[b] - 257, lens_q[b] - 1]
+        qs, ks = int(cu_q[b]), int(cu_k[b])
+        for h in (0, 9, 31):
+            g = h // (H_q // H_kv)
+            want = oracle.attention_head(f64(q[qs:qs + lens_q[b], h]), f64(k[ks:ks + lens_k[b], g]),
+                                         f64(v[ks:ks + lens_k[b], g]), 1.0 / np.sqrt(D), True, rows=rows)
+            assert G.max_err(got[qs + np.asarray(rows), h], want) <= G.TOL["bf16"], (b, h)

@@ -255,6 +255,7 @@ attn_status_t attn_fwd_prefill_varlen(const void* q, const void* k, const void* 
     a.window = window;
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
+    a.total_q = total_q;
     return hip_status(attn::launch_prefill_bf16(a, static_cast<hipStream_t>(stream)));
 }
 

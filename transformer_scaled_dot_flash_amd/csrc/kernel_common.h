@@ -203,6 +203,7 @@ struct PrefillArgs {
     int window;        // causal sliding window in keys (0: none)
     const int* cu_q;   // packed batch: [B + 1] row offsets of each sequence's
     const int* cu_k;   //   queries / keys (nullptr: contiguous [B][H][T][D])
+    int total_q;       // packed batch: rows of q (picks the launch shape)
 };
 
 // Paged KV cache of the decode kernel (block_table == nullptr: contiguous).

@@ -415,13 +415,17 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
 #define PF_FORCE 0
 #endif
 
-// Large problems (at least two 256-row workgroups per CU): 8 waves, one
-// workgroup per CU.  Otherwise 4 waves, two workgroups per CU.  Both use
-// 64 KiB of LDS (two K and two V tiles).
+// Long sequences with at least two 256-row workgroups per CU: 8 waves, one
+// workgroup per CU (one K/V tile in LDS serves 256 rows).  Otherwise 4
+// waves, two workgroups per CU: with short sequences the per-workgroup
+// start-up and the diagonal tiles weigh more, and 128-row workgroups were
+// measured faster (T = 512: 528 vs 446 TFLOP/s; T = 1024: 710 vs 650; equal
+// at T = 4096).  Both use 64 KiB of LDS (two K and two V tiles).
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
     const long long wg_big = (long long)a.B * a.H_q * ((a.T_q + 255) / 256);
-    const bool big = PF_FORCE == 2 || (PF_FORCE == 0 && wg_big >= 512);
+    const long long rows_per_seq = VARLEN ? a.total_q / (a.B > 0 ? a.B : 1) : a.T_q;
+    const bool big = PF_FORCE == 2 || (PF_FORCE == 0 && wg_big >= 512 && rows_per_seq >= 4096);
     if (big) return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 8, 2>(a, s);
     return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 4, 2>(a, s);
 }
