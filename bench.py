@@ -331,6 +331,32 @@ def time_paged_decode(abi, torch, wd, kd, vd, qd, od_contig, stream, dev, warmup
     }
 
 
+def qkv_projection_line(abi, torch, np, stream, dev, warmup, settle, steps):
+    """Fused QKV projection at the Llama-3-8B shape: 8192 tokens, d_model
+    4096, 32 q heads + 8 kv heads of 128 (N = 6144), bf16."""
+    from transformer_scaled_dot_flash_amd import inputs
+    B, T, dm, H_q, H_kv, D = 1, 8192, 4096, 32, 8, 128
+    N = (H_q + 2 * H_kv) * D
+
+    def mk(seed, shape):
+        bits = inputs.normal(seed, shape, "bf16")
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    x = mk(8001, (B * T, dm))
+    w = mk(8002, (N, dm))
+    q = torch.empty(B, H_q, T, D, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(B, H_kv, T, D, dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    flops = 2 * B * T * dm * N
+
+    def run():
+        abi.attn_qkv_project(x, w, q, k, v, B, T, dm, H_q, H_kv, D, abi.ATTN_BF16, stream)
+    log("qkv projection")
+    avg, mn = time_calls(torch, stream, run, warmup, settle, steps)
+    return mfma_line("fused QKV projection TFLOP/s",
+                     f"X [8192 x 4096] W [6144 x 4096] -> Q [1,32,8192,128], K, V [1,8,8192,128] bf16",
+                     flops, avg, mn, "qkv_project_kernel<128>")
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         # python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR COPY_MIB "commands"
@@ -347,7 +373,7 @@ def main():
                     help="time one part only (for profiling runs)")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV decode line")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the sliding-window and packed-batch prefill lines")
+                    help="skip the sliding-window, packed-batch and QKV-projection lines")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -440,6 +466,8 @@ def main():
         extra["window_prefill"] = window_prefill_line(abi, torch, wp, qp, kp, vp, stream, args.warmup,
                                                       args.settle, min(K, 20))
         extra["varlen_prefill"] = varlen_prefill_line(abi, torch, np, stream, dev, args.warmup,
+                                                      args.settle, min(K, 20))
+        extra["qkv_projection"] = qkv_projection_line(abi, torch, np, stream, dev, args.warmup,
                                                       args.settle, min(K, 20))
     paged = None
     if do_pg:

@@ -216,6 +216,31 @@ attn_status_t attn_fwd_decode_paged(const void* q, const void* k_pages, const vo
 size_t attn_fwd_decode_paged_workspace_bytes(int B, int H_q, int H_kv, int D, int page_size,
                                              int max_pages, int num_splits);
 
+/*
+ * Fused QKV projection, the step before the attention forward (Ch. 11 page,
+ * section 11.2: Q, K and V are three linear maps of the same input X;
+ * section 11.8.1: q heads and the fewer kv heads are column blocks of those
+ * maps).  One bf16 GEMM Y = X W^T over the concatenated weights; its epilogue
+ * splits the columns and writes Q, K, V in the layouts attn_fwd_prefill and
+ * attn_fwd_decode take.
+ *
+ *   x        device [B*T][d_model]: token t of sequence b is row b*T + t
+ *   w        device [(H_q + 2*H_kv)*D][d_model]: rows 0 .. H_q*D - 1 are W_Q
+ *            (row h*D + d gives feature d of q head h), then H_kv*D rows of
+ *            W_K, then H_kv*D rows of W_V (a linear layer's weight layout)
+ *   q        device [B][H_q][T][D], fully overwritten
+ *   k, v     device [B][H_kv][T][D], fully overwritten
+ *   d_model  a multiple of 64
+ *   dtype    ATTN_BF16 only
+ * Arithmetic: bf16 matrix cores, fp32 accumulation over d_model, each output
+ * rounded once to bf16 (round-to-nearest-even).  All pointers 16-byte
+ * aligned; the outputs may overlap neither each other nor the inputs.
+ * B == 0 or T == 0 is an empty problem (ATTN_OK, nothing launched).
+ */
+attn_status_t attn_qkv_project(const void* x, const void* w, void* q, void* k, void* v, int B,
+                               int T, int d_model, int H_q, int H_kv, int D, int dtype,
+                               void* stream);
+
 /* Workspace bytes attn_fwd_decode needs for these sizes (num_splits as
  * passed to attn_fwd_decode, 0 = default).  Returns 0 when no workspace is
  * needed (one split, or dtype ATTN_F32) and for invalid sizes. */

@@ -229,3 +229,27 @@ def test_varlen_empty_ok():
     assert varlen(mq=0, q=0, k=0, v=0, o=0, cq=0, ck=0) == OK
     assert varlen(total_q=0, q=0, k=0, v=0, o=0, cq=0, ck=0) == OK
     assert varlen(W=64, causal=1, cq=CQ + 4, ck=CK + 8, B=0) == OK
+
+
+# --- fused QKV projection ------------------------------------------------------------
+XP, WQ, QO, KO, VO = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def qkv(x=XP, w=WQ, q=QO, k=KO, v=VO, B=1, T=128, dm=256, H_q=8, H_kv=2, D=128, dtype=BF16):
+    return A.attn_qkv_project(x, w, q, k, v, B, T, dm, H_q, H_kv, D, dtype, None, check=False)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), SHAPE), (dict(T=-1), SHAPE), (dict(dm=0), SHAPE), (dict(H_kv=3), SHAPE),
+    (dict(T=1 << 20, dm=4096), SHAPE),
+    (dict(dm=96), UNSUP), (dict(D=96), UNSUP), (dict(dtype=F32), UNSUP),
+    (dict(x=0), NULL), (dict(v=0), NULL), (dict(w=WQ + 4), ALIGN),
+    (dict(q=XP), ALIAS), (dict(k=QO + 64), ALIAS), (dict(v=WQ + 256), ALIAS),
+])
+def test_qkv_rejects(kw, want):
+    assert qkv(**kw) == want
+
+
+def test_qkv_empty_ok():
+    assert qkv(B=0, x=0, w=0, q=0, k=0, v=0) == OK
+    assert qkv(T=0, x=0, w=0, q=0, k=0, v=0) == OK

@@ -40,6 +40,7 @@ EXPORTED = (
     "attn_fwd_decode_default_splits",
     "attn_fwd_decode_paged",
     "attn_fwd_decode_paged_workspace_bytes",
+    "attn_qkv_project",
     "attn_status_string",
     "attn_abi_version",
     "attn_last_hip_error",
@@ -90,6 +91,8 @@ def load_library(path: Path | str | None = None):
     lib.attn_fwd_decode_paged.restype = i
     lib.attn_fwd_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.attn_fwd_decode_paged_workspace_bytes.restype = sz
+    lib.attn_qkv_project.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.attn_qkv_project.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -182,6 +185,16 @@ def attn_fwd_decode_paged(q, k_pages, v_pages, o, block_table, seq_lens, B, H_q,
 def attn_fwd_decode_paged_workspace_bytes(B, H_q, H_kv, D, page_size, max_pages, num_splits=0) -> int:
     return int(load_library().attn_fwd_decode_paged_workspace_bytes(B, H_q, H_kv, D, page_size,
                                                                      max_pages, num_splits))
+
+
+def attn_qkv_project(x, w, q, k, v, B, T, d_model, H_q, H_kv, D, dtype, stream=None,
+                     check=True) -> int:
+    lib = load_library()
+    st = lib.attn_qkv_project(_ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), B, T, d_model, H_q, H_kv,
+                              D, dtype, _stream(stream))
+    if check:
+        _check(st, "attn_qkv_project")
+    return st
 
 
 def attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, dtype, num_splits=0) -> int:

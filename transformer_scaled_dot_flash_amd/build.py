@@ -25,13 +25,14 @@ INCLUDE = ROOT / "include"
 # inputs are never NaN; masked scores are -inf), which lets max/min skip NaN
 # canonicalisation.  The ABI layer, which validates inputs, is not.
 KERNEL_FLAGS = ["-fno-honor-nans"]
-KERNEL_SOURCES = {"prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip"}
+KERNEL_SOURCES = {"prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip", "qkv_bf16.hip"}
 
 HIP_SOURCES = [
     CSRC / "attn_api.hip",
     CSRC / "prefill_bf16.hip",
     CSRC / "prefill_f32.hip",
     CSRC / "decode_bf16.hip",
+    CSRC / "qkv_bf16.hip",
 ]
 HIP_HEADERS = [CSRC / "kernel_common.h", INCLUDE / "attn.h"]
 

@@ -395,6 +395,47 @@ size_t attn_fwd_decode_paged_workspace_bytes(int B, int H_q, int H_kv, int D, in
     return decode_ws_bytes(B, H_q, D, plan_splits(B, H_q, H_kv, max_pages * page_size, num_splits));
 }
 
+attn_status_t attn_qkv_project(const void* x, const void* w, void* q, void* k, void* v, int B,
+                               int T, int d_model, int H_q, int H_kv, int D, int dtype, void* stream) {
+    if (B < 0 || T < 0 || d_model <= 0 || H_q <= 0 || H_kv <= 0) return ATTN_ERR_INVALID_SHAPE;
+    if (H_q % H_kv != 0) return ATTN_ERR_INVALID_SHAPE;
+    if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (d_model % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+    const long long M = (long long)B * T, N = (long long)(H_q + 2 * H_kv) * D;
+    // every tensor is addressed with 32-bit byte offsets
+    if (M * d_model * 2 >= (1LL << 31) || N * d_model * 2 >= (1LL << 31) ||
+        M * H_q * D * 2 >= (1LL << 31) || (long long)d_model * 2 * 256 >= (1LL << 31))
+        return ATTN_ERR_INVALID_SHAPE;
+    if (M == 0) return ATTN_OK;
+    if (!x || !w || !q || !k || !v) return ATTN_ERR_NULL_PTR;
+    if (misaligned(x) || misaligned(w) || misaligned(q) || misaligned(k) || misaligned(v))
+        return ATTN_ERR_ALIGNMENT;
+    const size_t nx = (size_t)M * d_model * 2, nw = (size_t)N * d_model * 2;
+    const size_t nq = (size_t)M * H_q * D * 2, nkv = (size_t)M * H_kv * D * 2;
+    const void* outs[] = {q, k, v};
+    const size_t olen[] = {nq, nkv, nkv};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], olen[i], x, nx) || overlaps(outs[i], olen[i], w, nw)) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], olen[i], outs[j], olen[j])) return ATTN_ERR_ALIAS;
+    }
+    attn::QkvArgs a{};
+    a.x = x;
+    a.w = w;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.d_model = d_model;
+    a.T = T;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.D = D;
+    return hip_status(attn::launch_qkv_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";

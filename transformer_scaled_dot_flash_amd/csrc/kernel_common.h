@@ -230,10 +230,20 @@ struct DecodeArgs {
     PagedKV paged;       // paged cache (T_kv = max_pages * page_size), or all zero
 };
 
+struct QkvArgs {
+    const void* x;   // [M][d_model]
+    const void* w;   // [N][d_model], N = (H_q + 2 H_kv) D
+    void* q;         // [B][H_q][T][D]
+    void* k;         // [B][H_kv][T][D]
+    void* v;         // [B][H_kv][T][D]
+    int M, N, d_model, T, H_q, H_kv, D;
+};
+
 // Launchers return the HIP status of the launch call itself.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_qkv_bf16(const QkvArgs& a, hipStream_t s);
 
 template <typename Tup, size_t... I>
 inline void fill_ptrs(Tup& t, void** p, std::index_sequence<I...>) {

@@ -1,0 +1,190 @@
+// Fused QKV projection for gfx950: one bf16 GEMM Y = X W^T over the
+// concatenated projection weights, with an epilogue that splits the output
+// columns into Q, K and V and writes each in the head-major layout the
+// attention kernels read.
+//
+// Method (learn-cuda-from-scratch Ch. 11 "Attention", section 11.2: Q, K and
+// V are three linear maps of the same input X; section 11.8.1: the query
+// heads and the (fewer) kv heads are column blocks of those maps):
+//
+//     Y[m, n] = sum_k X[m, k] W[n, k]          m = token, n = output feature
+//     n <  H_q D            : Q[b, n / D,              t, n % D]
+//     n <  (H_q + H_kv) D   : K[b, (n - H_q D) / D,    t, n % D]
+//     otherwise             : V[b, (n - H_q D - H_kv D) / D, t, n % D]
+//
+// with m = b T + t.  W is stored [N][d_model] (one row per output feature,
+// the layout of a linear layer's weight), so both GEMM operands are
+// contiguous along the reduction dimension.
+//
+// gfx950 mapping:
+//   * 8 waves per workgroup, workgroup tile 256 tokens x 256 features, wave
+//     tile 64 tokens x 128 features.  Y^T = W X^T on
+//     v_mfma_f32_32x32x16_bf16 (A = 32 features x 16 k of W, B = 32 tokens x
+//     16 k of X): each lane's accumulator holds one token and 4-feature runs,
+//     so the epilogue writes 8-byte runs of one output row.  Every W
+//     fragment feeds 2 MFMAs and every X fragment 4 (0.75 KiB of LDS per
+//     MFMA).
+//   * 64-wide k tiles of X and W go HBM -> LDS with 16-byte buffer loads that
+//     write LDS directly, double buffered; 128-byte rows use the same XOR
+//     swizzle of 16-byte chunks as the attention kernels' K tiles (conflict-
+//     free ds_read_b128 operand reads).
+//   * Tokens past B T and features past N read as zero (range-checked buffer
+//     resources) and are not stored.  d_model must be a multiple of 64.
+#include "kernel_common.h"
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kTM = 256;   // tokens per workgroup
+constexpr int kTN = 256;   // features per workgroup
+constexpr int kTK = 64;    // reduction elements per k tile
+constexpr int kRowB = kTK * 2;                 // bytes per tile row (128)
+constexpr int kCPR = kRowB / 16;               // 16-byte chunks per row (8)
+constexpr int kXTile = kTM * kRowB;            // 32 KiB
+constexpr int kWTile = kTN * kRowB;            // 32 KiB
+constexpr int kStage = kXTile + kWTile;
+
+template <int D>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16* __restrict__ Qo,
+                   bf16* __restrict__ Ko, bf16* __restrict__ Vo, int M, int N, int d_model, int T,
+                   int H_q, int H_kv, int n_nt) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    const int wt = wave & 3;   // token block of 64
+    const int wf = wave >> 2;  // feature block of 128
+
+    const int mt = blockIdx.x / n_nt, nt = blockIdx.x - mt * n_nt;
+    const int m0 = mt * kTM, n0 = nt * kTN;
+
+    const uint32_t rowb = (uint32_t)d_model * 2;
+    const auto rX = make_rsrc(X + (size_t)m0 * d_model, (uint32_t)max(0, min(kTM, M - m0)) * rowb);
+    const auto rW = make_rsrc(W + (size_t)n0 * d_model, (uint32_t)max(0, min(kTN, N - n0)) * rowb);
+
+    // One k tile of X (256 rows) and of W (256 rows): 32 + 32 loads of
+    // 1 KiB, 4 + 4 per wave.
+    auto issue = [&](int kt, int buf) {
+        unsigned char* xs = smem + buf * kStage;
+        unsigned char* ws = xs + kXTile;
+        const uint32_t kb = (uint32_t)kt * kRowB;
+#pragma unroll
+        for (int n = 0; n < kXTile / (1024 * kWaves); ++n) {
+            const int blk = wave * (kXTile / (1024 * kWaves)) + n;
+            const int p = blk * 64 + lane;
+            const int row = p / kCPR;
+            const int logical = (p % kCPR) ^ swz<kCPR>(row);
+            buf_load_lds16(rX, xs + blk * 1024, (uint32_t)row * rowb + kb + logical * 16);
+            buf_load_lds16(rW, ws + blk * 1024, (uint32_t)row * rowb + kb + logical * 16);
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+        acc[fb][0] = f32x16{};
+        acc[fb][1] = f32x16{};
+    }
+
+    const int n_kt = d_model / kTK;
+    issue(0, 0);
+    // Lane offsets of the operand fragments within a tile: row l32 of the
+    // wave's block, chunk 2s + hi for k step s.
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        wait_vmem_all();
+        __syncthreads();  // tile kt landed for every wave; tile kt-1's buffer is free
+        if (kt + 1 < n_kt) issue(kt + 1, buf ^ 1);
+        const unsigned char* xs = smem + buf * kStage;
+        const unsigned char* ws = xs + kXTile;
+#pragma unroll
+        for (int s = 0; s < kTK / 16; ++s) {
+            bf16x8 xf[2], wfr[4];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int row = wt * 64 + tb * 32 + l32;
+                xf[tb] = *reinterpret_cast<const bf16x8*>(xs + row * kRowB + (((2 * s + hi) ^ swz<kCPR>(row)) * 16));
+            }
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+                const int row = wf * 128 + fb * 32 + l32;
+                wfr[fb] = *reinterpret_cast<const bf16x8*>(ws + row * kRowB + (((2 * s + hi) ^ swz<kCPR>(row)) * 16));
+            }
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wfr[fb], xf[tb], acc[fb][tb], 0, 0, 0);
+            }
+        }
+    }
+
+    // Epilogue: lane (token column l32, half hi) holds features
+    // 8 (j / 4) + 4 hi + j % 4 of each 32-feature block: runs of 4 features
+    // of one token, stored as 8 bytes.  A 32-feature block never straddles
+    // a head (D is 64 or 128).
+    const int qn = H_q * D, kn = H_kv * D;
+    const uint32_t q_bytes = (uint32_t)((size_t)M * qn * 2), kv_bytes = (uint32_t)((size_t)M * kn * 2);
+    const auto rQ = make_rsrc(Qo, q_bytes);
+    const auto rK = make_rsrc(Ko, kv_bytes);
+    const auto rV = make_rsrc(Vo, kv_bytes);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int m = m0 + wt * 64 + tb * 32 + l32;
+        const int b = m / T, t = m - b * T;
+        const bool m_ok = m < M;
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) {
+            const int nb = n0 + wf * 128 + fb * 32;  // first feature of the block (uniform)
+            if (nb >= N) continue;
+            int col, H;
+            __amdgpu_buffer_rsrc_t r = rQ;
+            if (nb < qn) {
+                col = nb;
+                H = H_q;
+            } else if (nb < qn + kn) {
+                col = nb - qn;
+                H = H_kv;
+                r = rK;
+            } else {
+                col = nb - qn - kn;
+                H = H_kv;
+                r = rV;
+            }
+            const int h = col / D, d0 = col - h * D;
+            const uint32_t base = (uint32_t)(((size_t)(b * H + h) * T + t) * D + d0) * 2;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                bf16x4 w;
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) w[r4] = (bf16)acc[fb][tb][4 * g4 + r4];
+                const uint32_t off = m_ok ? base + (uint32_t)(8 * g4 + 4 * hi) * 2 : 0xFFFFFFF0u;
+                buf_store_b64(__builtin_bit_cast(u32x2, w), r, off);
+            }
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_q(const QkvArgs& a, hipStream_t s) {
+    const int n_mt = (a.M + kTM - 1) / kTM;
+    const int n_nt = (a.N + kTN - 1) / kTN;
+    return launch_kernel(qkv_project_kernel<D>, dim3((unsigned)((long long)n_mt * n_nt)),
+                         dim3(64 * kWaves), 0, s, static_cast<const bf16*>(a.x),
+                         static_cast<const bf16*>(a.w), static_cast<bf16*>(a.q),
+                         static_cast<bf16*>(a.k), static_cast<bf16*>(a.v), a.M, a.N, a.d_model, a.T,
+                         a.H_q, a.H_kv, n_nt);
+}
+
+}  // namespace
+
+hipError_t launch_qkv_bf16(const QkvArgs& a, hipStream_t s) {
+    return a.D == 128 ? launch_q<128>(a, s) : launch_q<64>(a, s);
+}
+
+}  // namespace attn
