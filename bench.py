@@ -94,10 +94,30 @@ def cpu_baseline(budget_s=15.0):
 
 
 KERNELS = {
-    # name in profiles/ : (kernel-name substring, source files, algorithmic bytes per launch)
-    "prefill_bf16_T8192_D128_gqa": ("prefill_bf16_kernel", ["prefill_bf16.hip", "kernel_common.h"]),
-    "decode_bf16_B64_T4096_D128": ("decode_split_kernel", ["decode_bf16.hip", "kernel_common.h"]),
+    # name in profiles/ : (mangled kernel-name substring, source files)
+    # prefill<D=128, causal, contiguous, RB=1, BN=64, 8 waves>; decode<D=128, contiguous / paged>
+    "prefill_bf16_T8192_D128_gqa": ("prefill_bf16_kernelILi128ELb1ELb0ELi1ELi64ELi8E",
+                                    ["prefill_bf16.hip", "kernel_common.h"]),
+    "decode_bf16_B64_T4096_D128": ("decode_split_kernelILi128ELb0E", ["decode_bf16.hip", "kernel_common.h"]),
+    "decode_paged_bf16_B64_T4096_D128_page16": ("decode_split_kernelILi128ELb1E",
+                                                ["decode_bf16.hip", "kernel_common.h"]),
+    "qkv_project_bf16_T8192_dmodel4096_N6144": ("qkv_project_kernelILi128E", ["qkv_bf16.hip", "kernel_common.h"]),
 }
+
+
+def algorithmic_bytes(name):
+    from transformer_scaled_dot_flash_amd.workloads import DECODE_HEADLINE as wd
+    from transformer_scaled_dot_flash_amd.workloads import PREFILL_HEADLINE as wp
+    if name.startswith("prefill"):
+        return wp.bytes()
+    if name.startswith("decode_paged"):
+        return wd.bytes() + wd.B * (wd.T_kv // PAGE_SIZE) * 4 + wd.B * 4  # + block table and lengths
+    if name.startswith("decode"):
+        return wd.bytes()
+    if name.startswith("qkv"):
+        M, dm, N = 8192, 4096, 6144
+        return 2 * (M * dm + N * dm + M * N)  # X, W read once; Q, K, V written once
+    raise KeyError(name)
 
 
 def _csv_rows(path):
@@ -111,8 +131,6 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
     runs, FETCH_SIZE then WRITE_SIZE, each with a device copy of copy_mib MiB
     for calibration) into the summaries kept under profiles/."""
     import glob
-    from transformer_scaled_dot_flash_amd.workloads import DECODE_HEADLINE as wd
-    from transformer_scaled_dot_flash_amd.workloads import PREFILL_HEADLINE as wp
     stats = _csv_rows(glob.glob(f"{trace_dir}/**/*kernel_stats.csv", recursive=True)[0])
 
     def counter(d, name):
@@ -135,10 +153,10 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
     f_scale = copy_bytes / (f_copy * 1024.0)
     w_scale = copy_bytes / (w_copy * 1024.0)
     csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
-    algo = {"prefill_bf16_T8192_D128_gqa": wp.bytes(), "decode_bf16_B64_T4096_D128": wd.bytes()}
+    algo = {name: algorithmic_bytes(name) for name in KERNELS}
     for name, (sub, files) in KERNELS.items():
         st = [r for r in stats if sub in r["Name"]]
-        if not st:
+        if not st or pick(fetch, sub) is None or pick(write, sub) is None:
             continue
         st = st[0]
         fk, wk = pick(fetch, sub), pick(write, sub)
@@ -180,6 +198,14 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
 
 
 PAGE_SIZE = 16
+
+
+def profile_traffic(name):
+    """HBM bytes per launch from profiles/<name>_traffic.json, or None when the
+    kernel source changed since the counters were taken."""
+    _, files = KERNELS[name]
+    csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
+    return traffic_from_profile(name, source_digest([csrc / f for f in files]))
 WINDOW = 4096                 # sliding-window line: Mistral-style 4K window
 VARLEN_TOKENS = 32768         # packed-batch line: total query tokens
 
@@ -325,7 +351,8 @@ def time_paged_decode(abi, torch, wd, kd, vd, qd, od_contig, stream, dev, warmup
                    "bytes": nbytes},
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128, paged>",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": profile_traffic("decode_paged_bf16_B64_T4096_D128_page16"),
                      "avg_call_us": round(avg * 1e3, 2), "min_call_us": round(min(ms) * 1e3, 2)},
         "equals_contiguous_decode": same,
     }
@@ -352,9 +379,11 @@ def qkv_projection_line(abi, torch, np, stream, dev, warmup, settle, steps):
         abi.attn_qkv_project(x, w, q, k, v, B, T, dm, H_q, H_kv, D, abi.ATTN_BF16, stream)
     log("qkv projection")
     avg, mn = time_calls(torch, stream, run, warmup, settle, steps)
-    return mfma_line("fused QKV projection TFLOP/s",
+    line = mfma_line("fused QKV projection TFLOP/s",
                      f"X [8192 x 4096] W [6144 x 4096] -> Q [1,32,8192,128], K, V [1,8,8192,128] bf16",
                      flops, avg, mn, "qkv_project_kernel<128>")
+    line["roofline"]["traffic"] = profile_traffic("qkv_project_bf16_T8192_dmodel4096_N6144")
+    return line
 
 
 def main():
@@ -369,8 +398,8 @@ def main():
     ap.add_argument("--settle", type=float, default=1.0,
                     help="minimum seconds of untimed warm-up (GPU clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "paged"], default=None,
-                    help="time one part only (for profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "paged", "window", "varlen", "qkv"],
+                    default=None, help="time one part only (for profiling runs)")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV decode line")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the sliding-window, packed-batch and QKV-projection lines")
@@ -462,11 +491,14 @@ def main():
     d_gbs = wd.bytes() / (d_avg * 1e-3) / 1e9 if do_d else None
 
     extra = {}
-    if args.only is None and not args.no_extra:
+    all_extra = args.only is None and not args.no_extra
+    if all_extra or args.only == "window":
         extra["window_prefill"] = window_prefill_line(abi, torch, wp, qp, kp, vp, stream, args.warmup,
                                                       args.settle, min(K, 20))
+    if all_extra or args.only == "varlen":
         extra["varlen_prefill"] = varlen_prefill_line(abi, torch, np, stream, dev, args.warmup,
                                                       args.settle, min(K, 20))
+    if all_extra or args.only == "qkv":
         extra["qkv_projection"] = qkv_projection_line(abi, torch, np, stream, dev, args.warmup,
                                                       args.settle, min(K, 20))
     paged = None
