@@ -96,7 +96,7 @@ def cpu_baseline(budget_s=15.0):
 KERNELS = {
     # name in profiles/ : (mangled kernel-name substring, source files)
     # prefill<D=128, causal, contiguous, RB=1, BN=64, 8 waves>; decode<D=128, contiguous / paged>
-    "prefill_bf16_T8192_D128_gqa": ("prefill_bf16_kernelILi128ELb1ELb0ELi1ELi64ELi8E",
+    "prefill_bf16_T8192_D128_gqa": ("prefill_bf16_kernelILi128ELb1ELb0ELi1ELi128ELi8E",
                                     ["prefill_bf16.hip", "kernel_common.h"]),
     "decode_bf16_B64_T4096_D128": ("decode_split_kernelILi128ELb0E", ["decode_bf16.hip", "kernel_common.h"]),
     "decode_paged_bf16_B64_T4096_D128_page16": ("decode_split_kernelILi128ELb1E",
@@ -255,7 +255,7 @@ def window_prefill_line(abi, torch, wp, qp, kp, vp, stream, warmup, settle, step
     avg, mn = time_calls(torch, stream, run, warmup, settle, steps)
     return mfma_line("sliding-window prefill TFLOP/s",
                      f"causal GQA B=1 H_q=32 H_kv=8 T=8192 D=128 bf16, window {W}", flops, avg, mn,
-                     "prefill_bf16_kernel<128,64,causal> (window)")
+                     "prefill_bf16_kernel<D=128,causal,BN=128,8 waves> (window)")
 
 
 def varlen_prefill_line(abi, torch, np, stream, dev, warmup, settle, steps):
@@ -288,7 +288,7 @@ def varlen_prefill_line(abi, torch, np, stream, dev, warmup, settle, steps):
     line = mfma_line("packed variable-length prefill TFLOP/s",
                      f"{len(lens)} causal GQA sequences, lengths U[128, 4096] (seed 2024), "
                      f"{total} tokens, H_q=32 H_kv=8 D=128 bf16", flops, avg, mn,
-                     "prefill_bf16_kernel<128,64,causal,packed>")
+                     "prefill_bf16_kernel<D=128,causal,packed,BN=64,4 waves>")
     line["config"]["lengths"] = lens
     return line
 
@@ -544,7 +544,7 @@ def main():
     if do_p:
         result["roofline"] = {
             "bound": "mfma",
-            "kernel": "prefill_bf16_kernel<128,64,causal>",
+            "kernel": "prefill_bf16_kernel<D=128,causal,BN=128,8 waves>",
             "achieved": round(p_tflops, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

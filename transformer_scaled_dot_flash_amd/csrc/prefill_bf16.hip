@@ -25,11 +25,13 @@
 //     an XOR swizzle of the 16-byte chunks (chosen through the per-lane
 //     source address) keeps the K reads and the transposing V reads free of
 //     bank conflicts on the 64-bank LDS.
-//   * Per wave, the scores of key tile t+1 are issued on the matrix cores in
-//     the same basic block that forms tile t's weights on the vector ALUs.
-//     K therefore runs one tile ahead of V: LDS holds two K tiles (t+1 being
-//     read, t+2 loading) and two V tiles (t being read, t+1 loading).  The
-//     loop is unrolled by two so both ring slots are compile-time offsets.
+//   * Each step handles one key tile: scores, weights, O += P V.  The two
+//     waves on each SIMD overlap one another's matrix-core and vector work;
+//     computing the next tile's scores inside the current step (a software
+//     pipeline within the wave) measured slower and needs twice the score
+//     registers.  LDS holds two K and two V tiles (tile t being read, t+1
+//     loading); the loop is unrolled by two so both slots are compile-time
+//     offsets.
 //   * The V^T reads are issued as inline assembly (see ds_read_tr16_asm) so
 //     the compiler does not stall them behind the tile prefetches.
 //   * Softmax in the exp2 domain: the row maximum is taken on raw scores,
@@ -47,9 +49,9 @@
 //     head run on one XCD so its K/V stay in that XCD's L2.
 //
 // Configurations (RB = 1, two waves per SIMD): 8 waves x 32 rows per
-// workgroup for large problems (one K/V tile in LDS serves 256 query rows,
-// one workgroup per CU), 4 waves x 32 rows for small ones (twice as many
-// workgroups, two per CU).  RB = 2 halves the LDS read traffic per
+// workgroup and 128-key tiles for long sequences (one K/V tile in LDS serves
+// 256 query rows, one workgroup per CU), 4 waves x 32 rows and 64-key tiles
+// otherwise (two workgroups per CU).  RB = 2 halves the LDS read traffic per
 // FLOP but needs ~480 registers per lane, i.e. one wave per SIMD, and was
 // measured slower (the accumulators spill between AGPRs and VGPRs).
 #include "kernel_common.h"
@@ -67,8 +69,12 @@ __device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt,
     const int units = B * H_kv;  // (batch, kv head) pairs
     int qt_rev, unit, g;
     if ((units & 7) == 0) {
-        // Dispatch sends workgroup id to XCD (id mod 8).  Give each XCD a
-        // contiguous block of kv heads; within it, heaviest query tile first.
+        // Dispatch sends workgroup id to XCD (id mod 8).  Every workgroup of
+        // one (batch, kv head) unit goes to the XCD unit mod 8, so the unit's
+        // K/V is read through one L2; units are dealt to the XCDs in turn, so
+        // each XCD holds the same kv head of every sequence (in a packed batch
+        // of unequal lengths, contiguous blocks of units left one XCD with
+        // over twice the mean work).  Within an XCD, heaviest query tile first.
         const int xcd = id & 7;
         const int slot = id >> 3;
         const int upx = units >> 3;
@@ -76,7 +82,7 @@ __device__ inline TileCoord map_tile(int id, int B, int H_q, int H_kv, int n_qt,
         qt_rev = slot / per;
         const int rem = slot - qt_rev * per;
         const int u = rem / G;
-        unit = xcd * upx + u;
+        unit = u * 8 + xcd;
         g = rem - u * G;
     } else {
         const int per = units * G;
@@ -230,14 +236,12 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     auto issue_k = [&](int t) { issue(rK, kring + ((t - t_lo) & 1) * TILE, t); };
     auto issue_v = [&](int t) { issue(rV, vring + ((t - t_lo) & 1) * TILE, t); };
 
-    // Prologue: K(t_lo), V(t_lo), K(t_lo+1).  Step t then issues K(t+2) into
-    // K(t)'s slot and V(t+1) into V(t-1)'s slot, both read for the last time
-    // in step t-1.
+    // Prologue: K(t_lo), V(t_lo).  Step t issues K(t+1), V(t+1) into the
+    // slots of tile t-1, read for the last time in step t-1.
     if (t_lo < n_kt) {
         issue_k(t_lo);
         issue_v(t_lo);
     }
-    if (t_lo + 1 < n_kt) issue_k(t_lo + 1);
 
     f32x16 oacc[RB][D / 32];
     float m_use[RB];  // base of the exponent (log2 units), per row
@@ -255,33 +259,25 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     uint32_t voff[2][D / 32];           // V^T read offsets within a tile
     pv_lane_offsets<D>(voff, lane);
 
-    STile<BN, RB> s_a, s_b;  // scores of the current and the next tile, alternating
-    if (t_lo < n_kt) {
-        wait_vmem_all();
-        __syncthreads();
-        if (wave_live(t_lo * BN)) score_tile<D, BN, RB>(s_a, kring, qf, l32, hi);
-    }
+    STile<BN, RB> s_cur;  // scores of the current tile
 
-    // Step t with PAR = (t - t_lo) & 1 known at compile time: K(t+1) sits in
-    // slot 1 - PAR, V(t) in slot PAR.  s_cur holds the scores of tile t,
-    // s_next receives those of tile t+1.
-    auto step = [&](int t, auto par, STile<BN, RB>& s_cur, STile<BN, RB>& s_next) {
+    // Step t with PAR = (t - t_lo) & 1 known at compile time: K(t) and V(t)
+    // sit in slot PAR.
+    auto step = [&](int t, auto par) {
         constexpr int PAR = decltype(par)::value;
         const int j0 = t * BN;
-        // K(t+1) and V(t), issued one iteration ago, must be complete in LDS
-        // (for every wave's loads), and every wave must be done reading K(t-1)
-        // and V(t-1), whose stages are refilled below.
+        // K(t) and V(t), issued one step ago, must be complete in LDS (for
+        // every wave's loads), and every wave must be done reading K(t-1) and
+        // V(t-1), whose slots are refilled below.
         wait_vmem_all();
         __syncthreads();
-        if (t + 2 < n_kt) issue_k(t + 2);
-        if (t + 1 < n_kt) issue_v(t + 1);
-        if (j0 >= wave_kv_end) return;  // this and all later tiles are above the diagonal
-        if (j0 + BN <= wave_kv_begin) {
-            // Left of this wave's window.  If the next tile is its first, its
-            // scores are needed in the next step.
-            if (wave_live(j0 + BN)) score_tile<D, BN, RB>(s_next, kring + (1 - PAR) * TILE, qf, l32, hi);
-            return;
+        if (t + 1 < n_kt) {
+            issue_k(t + 1);
+            issue_v(t + 1);
         }
+        // Tiles above the diagonal or left of this wave's window: nothing to do.
+        if (!wave_live(j0)) return;
+        score_tile<D, BN, RB>(s_cur, kring + PAR * TILE, qf, l32, hi);
 
         // Per row block: mask, base update.
 #pragma unroll
@@ -330,12 +326,6 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             }
         }
 
-        // One straight-line block: the scores of tile t+1 go to the matrix
-        // cores while the weights of tile t are formed on the vector ALUs,
-        // then O += P V for tile t.  (After the wave's last tile the
-        // next-scores read a stale stage and are discarded.)
-        score_tile<D, BN, RB>(s_next, kring + (1 - PAR) * TILE, qf, l32, hi);
-
         bf16x8 pb[RB][BN / 16];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -373,8 +363,8 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         pv_tile<D, BN / 16, RB>(oacc, pb, va);
     };
     for (int t = t_lo; t < n_kt; t += 2) {
-        step(t, std::integral_constant<int, 0>{}, s_a, s_b);
-        if (t + 1 < n_kt) step(t + 1, std::integral_constant<int, 1>{}, s_b, s_a);
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_kt) step(t + 1, std::integral_constant<int, 1>{});
     }
 
     // Epilogue: O = O_acc / l, rounded once to bf16.  Rows past T_q fall
@@ -415,18 +405,19 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
 #define PF_FORCE 0
 #endif
 
-// Long sequences with at least two 256-row workgroups per CU: 8 waves, one
-// workgroup per CU (one K/V tile in LDS serves 256 rows).  Otherwise 4
-// waves, two workgroups per CU: with short sequences the per-workgroup
-// start-up and the diagonal tiles weigh more, and 128-row workgroups were
-// measured faster (T = 512: 528 vs 446 TFLOP/s; T = 1024: 710 vs 650; equal
-// at T = 4096).  Both use 64 KiB of LDS (two K and two V tiles).
+// Long sequences with at least two 256-row workgroups per CU: 8 waves and
+// 128-key tiles, one workgroup per CU (one K/V tile in LDS serves 256 rows;
+// 128 KiB of LDS; twice the keys per barrier than 64-key tiles, +3%).
+// Otherwise 4 waves and 64-key tiles, two workgroups per CU (64 KiB each):
+// with short sequences the per-workgroup start-up and the diagonal tiles
+// weigh more, and 128-row workgroups were measured faster (T = 512: 528 vs
+// 446 TFLOP/s; T = 1024: 710 vs 650; equal at T = 4096).
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
     const long long wg_big = (long long)a.B * a.H_q * ((a.T_q + 255) / 256);
     const long long rows_per_seq = VARLEN ? a.total_q / (a.B > 0 ? a.B : 1) : a.T_q;
     const bool big = PF_FORCE == 2 || (PF_FORCE == 0 && wg_big >= 512 && rows_per_seq >= 4096);
-    if (big) return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 8, 2>(a, s);
+    if (big) return launch_cfg<D, CAUSAL, VARLEN, 1, 128, 8, 2>(a, s);
     return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 4, 2>(a, s);
 }
 
