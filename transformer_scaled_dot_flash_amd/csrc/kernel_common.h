@@ -63,6 +63,26 @@ __device__ inline bf16x4 ds_read_tr16_asm(uint32_t lds_addr) {
     return r;
 }
 
+// ds_read_b128 as inline assembly, for reads that must stay in flight a
+// fixed distance ahead of their use (the compiler's scheduler sinks
+// intrinsic reads next to their first use when registers are tight).  Same
+// contract as ds_read_tr16_asm: the result may only be used after a wait
+// that binds it (lds_wait_bind1).
+template <int OFF>
+__device__ inline bf16x8 ds_read_b128_asm(uint32_t lds_addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
+    bf16x8 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "n"(OFF) : "memory");
+    return r;
+}
+
+// s_waitcnt lgkmcnt(N) binding one 16-byte fragment (see lds_wait_bind).
+template <int N>
+__device__ inline void lds_wait_bind1(bf16x8& f) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "n"(N));
+}
+
 // s_waitcnt lgkmcnt(N) that also redefines the fragments f, so no use of f
 // can be scheduled before it.  LDS operations complete in issue order, so
 // once at most N are outstanding, every read issued before the last N has

@@ -106,29 +106,66 @@ struct STile {
 };
 
 // S^T = K Q^T for one tile: RB * BN/32 independent MFMA chains over the D/16
-// feature steps; each K fragment (one ds_read_b128) feeds RB MFMAs.
-template <int D, int BN, int RB>
-__device__ inline void score_tile(STile<BN, RB>& st, const unsigned char* kst,
-                                  const bf16x8 (&qf)[RB][D / 16], int l32, int hi) {
-    constexpr int CPR = D / 8;
-    constexpr int ROWB = D * 2;
+// feature steps; each K fragment (one ds_read_b128) feeds RB MFMAs.  The
+// fragments are read KP MFMA groups ahead of their use through a ring of
+// KP + 1 registers (a slot is refilled one group after its last reader), so
+// every read has KP groups of matrix-core time to land.
+//
+// Fragment (s, kb) of lane (l32, hi) is 16-byte chunk (2s + hi) ^ swz(key)
+// of key kb * 32 + l32.  swz depends on the key's low 4 bits only, and 2s
+// and hi occupy disjoint bits, so the chunk is (hi ^ swz(l32)) ^ 2s: the
+// lane's address for step s is a0 ^ 32s (a0 = its step-0 address; rows are
+// 256-byte aligned, so the xor stays inside the row), and key block kb adds
+// the immediate kb * 32 rows.
+#ifndef PF_KP
+#define PF_KP 4
+#endif
+template <int D, int BN, int RB, int KOFF, int I>
+__device__ __attribute__((always_inline)) inline bf16x8 score_read(uint32_t a0) {
+    constexpr int NKB = BN / 32;
+    return ds_read_b128_asm<KOFF + (I % NKB) * 32 * D * 2>(a0 ^ (uint32_t)(32 * (I / NKB)));
+}
+template <int D, int BN, int RB, int KOFF, int KP, int I>
+__device__ __attribute__((always_inline)) inline void score_group(STile<BN, RB>& st, bf16x8 (&f)[KP + 1],
+                                                                  uint32_t a0,
+                                                                  const bf16x8 (&qf)[RB][D / 16]) {
+    constexpr int NKB = BN / 32;
+    constexpr int NM = NKB * (D / 16);
+    if constexpr (I + KP < NM) f[(I + KP) % (KP + 1)] = score_read<D, BN, RB, KOFF, I + KP>(a0);
+    constexpr int AFTER = (NM - 1 - I) < KP ? (NM - 1 - I) : KP;  // reads issued after read I
+    lds_wait_bind1<AFTER>(f[I % (KP + 1)]);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+        st.acc[rb][I % NKB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[I % (KP + 1)], qf[rb][I / NKB], st.acc[rb][I % NKB], 0, 0, 0);
+}
+template <int D, int BN, int RB, int KOFF, int KP, int... I>
+__device__ __attribute__((always_inline)) inline void score_groups(STile<BN, RB>& st, bf16x8 (&f)[KP + 1],
+                                                                   uint32_t a0,
+                                                                   const bf16x8 (&qf)[RB][D / 16],
+                                                                   std::integer_sequence<int, I...>) {
+    (score_group<D, BN, RB, KOFF, KP, I>(st, f, a0, qf), ...);
+}
+template <int D, int BN, int RB, int KOFF, int KP, int... P>
+__device__ __attribute__((always_inline)) inline void score_prologue(bf16x8 (&f)[KP + 1], uint32_t a0,
+                                                                     std::integer_sequence<int, P...>) {
+    ((f[P] = score_read<D, BN, RB, KOFF, P>(a0)), ...);
+}
+// a0: lane's step-0 address in K slot 0; KOFF: byte offset of the slot.
+template <int D, int BN, int RB, int KOFF>
+__device__ __attribute__((always_inline)) inline void score_tile(STile<BN, RB>& st, uint32_t a0,
+                                                                 const bf16x8 (&qf)[RB][D / 16]) {
+    constexpr int NM = (BN / 32) * (D / 16);
+    constexpr int KP = PF_KP < NM - 1 ? PF_KP : NM - 1;
+    static_assert(KP >= 1 && KP < NM && KP <= 15, "prefetch depth");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) st.acc[rb][kb] = f32x16{};
     }
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-            const int key = kb * 32 + l32;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                kst + key * ROWB + (((2 * s + hi) ^ swz<CPR>(key)) * 16));
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                st.acc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][s], st.acc[rb][kb], 0, 0, 0);
-        }
-    }
+    bf16x8 f[KP + 1];
+    score_prologue<D, BN, RB, KOFF, KP>(f, a0, std::make_integer_sequence<int, KP>{});
+    score_groups<D, BN, RB, KOFF, KP>(st, f, a0, qf, std::make_integer_sequence<int, NM>{});
 }
 
 template <int D, bool CAUSAL, bool VARLEN, int RB, int BN, int WAVES, int WPE>
@@ -260,6 +297,8 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     pv_lane_offsets<D>(voff, lane);
 
     STile<BN, RB> s_cur;  // scores of the current tile
+    // Step-0 address of this lane's K fragments in K slot 0 (see score_tile).
+    const uint32_t ka0 = lds_u32(kring) + (uint32_t)(l32 * ROWB + ((hi ^ swz<CPR>(l32)) << 4));
 
     // Step t with PAR = (t - t_lo) & 1 known at compile time: K(t) and V(t)
     // sit in slot PAR.
@@ -277,7 +316,7 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         }
         // Tiles above the diagonal or left of this wave's window: nothing to do.
         if (!wave_live(j0)) return;
-        score_tile<D, BN, RB>(s_cur, kring + PAR * TILE, qf, l32, hi);
+        score_tile<D, BN, RB, PAR * TILE>(s_cur, ka0, qf);
 
         // Per row block: mask, base update.
 #pragma unroll
