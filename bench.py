@@ -39,6 +39,13 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def percentiles_us(ms, what):
+    """p10 / median / p90 of per-launch times given in milliseconds, in us."""
+    t = sorted(ms)
+    pick = lambda q: round(t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))] * 1e3, 2)
+    return {f"p10_{what}_us": pick(0.1), f"median_{what}_us": pick(0.5), f"p90_{what}_us": pick(0.9)}
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -195,6 +202,52 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
               f"| source sha256 (kernel + common header) | `{digest[:16]}...` |", ""]
         (PROFILES / f"{name}.md").write_text("\n".join(md))
         print(f"wrote profiles/{name}.md")
+
+
+def summarize_counters(dirs, command_note, name="prefill_bf16_T8192_D128_gqa"):
+    """Shader-counter summary of one kernel from rocprofv3 --pmc runs (each a
+    directory of CSV output): averages per dispatch, plus the derived shader
+    clock (GRBM_GUI_ACTIVE is summed over the 8 XCDs) and the fraction of SIMD
+    cycles the matrix cores were busy."""
+    import glob
+    sub = KERNELS[name][0]
+    per = {}
+    dur = {}
+    for d in dirs:
+        for r in _csv_rows(glob.glob(f"{d}/**/*counter_collection.csv", recursive=True)[0]):
+            if sub not in r["Kernel_Name"]:
+                continue
+            key = (d, r["Dispatch_Id"])
+            per.setdefault(r["Counter_Name"], {}).setdefault(key, 0.0)
+            per[r["Counter_Name"]][key] += float(r["Counter_Value"])
+            dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    avg = {c: sum(v.values()) / len(v) for c, v in per.items()}
+    n_simd = 1024
+    gui = {k: v / 8 for k, v in per["GRBM_GUI_ACTIVE"].items()}  # cycles per XCD
+    ghz = sum(gui[k] / dur[k] for k in gui) / len(gui)
+    cyc = sum(gui.values()) / len(gui)
+    rows = [f"| {c} | {avg[c]:.4g} |" for c in sorted(avg)]
+    derived = [
+        f"| dispatches sampled | {len(gui)} |",
+        f"| kernel duration under counters | {sum(dur.values()) / len(dur) / 1e3:.1f} us |",
+        f"| shader cycles per launch (GRBM_GUI_ACTIVE / 8 XCDs) | {cyc:.0f} |",
+        f"| shader clock while it runs | {ghz:.2f} GHz |",
+    ]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        derived.append(f"| matrix cores busy (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {n_simd} SIMDs)) | "
+                       f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * n_simd):.3f} |")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+        derived.append(f"| VALU issued while matrix cores busy (fraction of busy cycles) | "
+                       f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.3f} |")
+    if "SQ_LDS_BANK_CONFLICT" in avg:
+        derived.append(f"| LDS bank-conflict cycles / LDS active cycles | "
+                       f"{avg['SQ_LDS_BANK_CONFLICT'] / max(avg['SQ_LDS_IDX_ACTIVE'], 1):.4f} |")
+    md = [f"# {name}: shader counters", "", f"Kernel: `{sub}...`", "",
+          "Commands (from the repository root on the GPU host):", "", "```", command_note, "```", "",
+          "| derived | value |", "|---|---|", *derived, "",
+          "| counter (sum over instances, average per dispatch) | value |", "|---|---|", *rows, ""]
+    (PROFILES / f"{name}_counters.md").write_text("\n".join(md))
+    print(f"wrote profiles/{name}_counters.md")
 
 
 PAGE_SIZE = 16
@@ -387,6 +440,10 @@ def qkv_projection_line(abi, torch, np, stream, dev, warmup, settle, steps):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # python bench.py --summarize-counters "commands" DIR [DIR ...]
+        summarize_counters(sys.argv[3:], sys.argv[2])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         # python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR COPY_MIB "commands"
         summarize(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6])
@@ -552,6 +609,7 @@ def main():
             "traffic": traffic_from_profile("prefill_bf16_T8192_D128_gqa", prefill_digest),
             "avg_launch_us": round(p_avg * 1e3, 2),
             "min_launch_us": round(min(p_ms) * 1e3, 2),
+            **percentiles_us(p_ms, "launch"),
         }
     if do_d:
         result["decode"] = {
@@ -568,6 +626,7 @@ def main():
                 "traffic": traffic_from_profile("decode_bf16_B64_T4096_D128", decode_digest),
                 "avg_call_us": round(d_avg * 1e3, 2),
                 "min_call_us": round(min(d_ms) * 1e3, 2),
+                **percentiles_us(d_ms, "call"),
             },
         }
     if paged is not None:
