@@ -14,8 +14,9 @@
 //     lane column and 16 keys per lane, so the row maximum is in-lane plus
 //     one exchange with lane^32.  Every K fragment read from LDS feeds RB
 //     MFMAs, and so does every V fragment: LDS read traffic per FLOP falls
-//     as 1/RB.  (LDS delivers about 128 B/clock per CU, exactly what one
-//     32x32x16 MFMA per SIMD per 32 clocks consumes at RB = 1.)
+//     as 1/RB.  (At RB = 1 one 32x32x16 MFMA per SIMD per 32 clocks
+//     consumes 128 B/clock per CU of LDS reads; LDS was measured to deliver
+//     about 139 B/clock per CU to 8 waves.)
 //   * The score accumulator layout is the B operand of O^T = V^T * P^T:
 //     weights are rounded to bf16 in place and never move between lanes.
 //     The V^T A operand comes straight from the row-major V tile with the
@@ -32,8 +33,12 @@
 //     registers.  LDS holds two K and two V tiles (tile t being read, t+1
 //     loading); the loop is unrolled by two so both slots are compile-time
 //     offsets.
-//   * The V^T reads are issued as inline assembly (see ds_read_tr16_asm) so
-//     the compiler does not stall them behind the tile prefetches.
+//   * The K fragments of the score phase are read four MFMA groups ahead of
+//     their use, the V^T fragments one key step ahead, both as inline
+//     assembly with waits bound to the fragment registers (see score_tile,
+//     pv_tile): the compiler otherwise keeps too few reads in flight and
+//     stalls the V^T reads behind the tile prefetches.  The P V MFMAs issue
+//     at raised wave priority.
 //   * Softmax in the exp2 domain: the row maximum is taken on raw scores,
 //     one FMA forms score * scale * log2(e) - base, and the base is only
 //     moved when a row's maximum grows by more than 8 (so weights stay
@@ -45,15 +50,18 @@
 //     the diagonal or the end of the keys pay for the element mask (Ch. 11
 //     "Attention" page, section 11.8.3), using exact tile bounds.
 //   * Workgroups run heaviest query tile first (causal work grows along the
-//     sequence) and, when the kv-head count allows, all workgroups of one kv
-//     head run on one XCD so its K/V stay in that XCD's L2.
+//     sequence) and, when the kv-head count allows, all workgroups of one
+//     (batch, kv head) run on one XCD so its K/V stay in that XCD's L2; the
+//     units are dealt to the XCDs in turn so unequal sequences of a packed
+//     batch spread evenly.
 //
 // Configurations (RB = 1, two waves per SIMD): 8 waves x 32 rows per
 // workgroup and 128-key tiles for long sequences (one K/V tile in LDS serves
 // 256 query rows, one workgroup per CU), 4 waves x 32 rows and 64-key tiles
 // otherwise (two workgroups per CU).  RB = 2 halves the LDS read traffic per
-// FLOP but needs ~480 registers per lane, i.e. one wave per SIMD, and was
-// measured slower (the accumulators spill between AGPRs and VGPRs).
+// FLOP but needs more than 256 registers per lane, i.e. one wave per SIMD,
+// and was measured slower: a single wave cannot overlap its own softmax with
+// its MFMAs the way two waves of a SIMD overlap each other's.
 #include "kernel_common.h"
 
 namespace attn {
@@ -114,12 +122,11 @@ struct STile {
 // Fragment (s, kb) of lane (l32, hi) is 16-byte chunk (2s + hi) ^ swz(key)
 // of key kb * 32 + l32.  swz depends on the key's low 4 bits only, and 2s
 // and hi occupy disjoint bits, so the chunk is (hi ^ swz(l32)) ^ 2s: the
-// lane's address for step s is a0 ^ 32s (a0 = its step-0 address; rows are
-// 256-byte aligned, so the xor stays inside the row), and key block kb adds
-// the immediate kb * 32 rows.
-#ifndef PF_KP
-#define PF_KP 4
-#endif
+// lane's address for step s is a0 ^ 32s (a0 = its step-0 address; rows
+// start at multiples of the row size D * 2 and the xor only changes bits
+// below it), and key block kb adds the immediate kb * 32 rows.  Four groups
+// ahead measured best (two: -1%, six or eight: no better).
+constexpr int kScoreReadAhead = 4;
 template <int D, int BN, int RB, int KOFF, int I>
 __device__ __attribute__((always_inline)) inline bf16x8 score_read(uint32_t a0) {
     constexpr int NKB = BN / 32;
@@ -156,7 +163,7 @@ template <int D, int BN, int RB, int KOFF>
 __device__ __attribute__((always_inline)) inline void score_tile(STile<BN, RB>& st, uint32_t a0,
                                                                  const bf16x8 (&qf)[RB][D / 16]) {
     constexpr int NM = (BN / 32) * (D / 16);
-    constexpr int KP = PF_KP < NM - 1 ? PF_KP : NM - 1;
+    constexpr int KP = kScoreReadAhead < NM - 1 ? kScoreReadAhead : NM - 1;
     static_assert(KP >= 1 && KP < NM && KP <= 15, "prefetch depth");
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -445,10 +452,6 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
                          a.neg_q, a.window, a.cu_q, a.cu_k);
 }
 
-#ifndef PF_FORCE
-#define PF_FORCE 0
-#endif
-
 // Long sequences with at least two 256-row workgroups per CU: 8 waves and
 // 128-key tiles, one workgroup per CU (one K/V tile in LDS serves 256 rows;
 // 128 KiB of LDS; twice the keys per barrier than 64-key tiles, +3%).
@@ -460,7 +463,7 @@ template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
     const long long wg_big = (long long)a.B * a.H_q * ((a.T_q + 255) / 256);
     const long long rows_per_seq = VARLEN ? a.total_q / (a.B > 0 ? a.B : 1) : a.T_q;
-    const bool big = PF_FORCE == 2 || (PF_FORCE == 0 && wg_big >= 512 && rows_per_seq >= 4096);
+    const bool big = wg_big >= 512 && rows_per_seq >= 4096;
     if (big) return launch_cfg<D, CAUSAL, VARLEN, 1, 128, 8, 2>(a, s);
     return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 4, 2>(a, s);
 }
