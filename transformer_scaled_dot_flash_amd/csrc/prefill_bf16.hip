@@ -351,13 +351,18 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             // the row lives in lane ^ 32).  The base only moves when some
             // lane's maximum exceeds it by more than 8; only then are the two
             // halves exchanged, so both lanes of a row share one base.
-            float mx = -INFINITY;
+            // Two independent chains of three-input maxima (v_max3_f32, two
+            // new values per instruction).
+            float mxa = -INFINITY, mxb = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-                for (int j = 0; j < 16; j += 2)
-                    mx = fmaxf(mx, fmaxf(s_cur.acc[rb][kb][j], s_cur.acc[rb][kb][j + 1]));
+                for (int j = 0; j < 16; j += 4) {
+                    mxa = fmaxf(fmaxf(mxa, s_cur.acc[rb][kb][j]), s_cur.acc[rb][kb][j + 1]);
+                    mxb = fmaxf(fmaxf(mxb, s_cur.acc[rb][kb][j + 2]), s_cur.acc[rb][kb][j + 3]);
+                }
             }
+            const float mx = fmaxf(mxa, mxb);
             if (__any(mx * c > m_use[rb] + 8.f)) {
                 const float m_row = fmaxf(mx, swap_halves(mx, xaddr)) * c;  // -inf: no visible key yet
                 const float m_t = fmaxf(m_use[rb], m_row);
