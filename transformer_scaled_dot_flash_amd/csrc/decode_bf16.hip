@@ -25,6 +25,8 @@
 // straight into its own LDS ring of kStages tiles with 16-byte buffer loads
 // (each 1 KiB load covers four whole rows), keeping kStages - 1 tiles in
 // flight while it consumes one; waves never synchronise with each other.
+// The cache is read exactly once per call, so these loads carry the
+// non-temporal hint (6.15 -> 6.7 TB/s contiguous, 5.9 -> 6.5 paged).
 //
 // Paged KV cache (the serving form; Ch. 11 page, section 11.11 on KV-cache
 // pages of 16 tokens and the block table that maps (request, token / 16) to
@@ -140,8 +142,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                 const bool second = ((key_t + n * (64 / CPR)) >> pg.page_shift) != pa;
                 const uint32_t boff =
                     (uint32_t)((key_t + row) & (page_size - 1)) * ROWB + logical * 16;
-                buf_load_lds16(second ? kB : kA, kst + n * 1024, boff);
-                buf_load_lds16(second ? vB : vA, vst + n * 1024, boff);
+                buf_load_lds16_nt(second ? kB : kA, kst + n * 1024, boff);
+                buf_load_lds16_nt(second ? vB : vA, vst + n * 1024, boff);
             }
         } else {
 #pragma unroll
@@ -150,8 +152,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
                 const int row = p / CPR;
                 const int logical = (p % CPR) ^ swz<CPR>(row);
                 const uint32_t boff = (uint32_t)(t * kBN + row) * ROWB + logical * 16;
-                buf_load_lds16(rK, kst + n * 1024, boff);
-                buf_load_lds16(rV, vst + n * 1024, boff);
+                buf_load_lds16_nt(rK, kst + n * 1024, boff);
+                buf_load_lds16_nt(rV, vst + n * 1024, boff);
             }
         }
     };
