@@ -44,7 +44,9 @@ namespace attn {
 namespace {
 
 constexpr int kBN = 32;     // keys per tile
-constexpr int kStages = 2;  // LDS ring depth per wave: one tile in flight while one is consumed
+// LDS ring depth per wave: two tiles in flight while one is consumed (with
+// the non-temporal loads: +1.5% contiguous, +1% paged over a 2-deep ring).
+constexpr int kStages = 3;
 
 // Wait until tile t of the ring has landed: `ahead` later tiles (PER loads
 // each) may still be in flight.  Loads complete in issue order.
@@ -246,9 +248,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         l_run += ps0 + ps1;
 
         // O^T += V^T P^T over the tile's two key steps.  With a contiguous
-        // cache this wave's next tile is drained first (measured 6.1 TB/s
-        // against 5.9 without); with pages it is left in flight (5.8
-        // against 5.3 TB/s): the scattered 4 KiB page reads need the overlap.
+        // cache this wave's tiles in flight are drained first (with plain
+        // loads 6.1 TB/s against 5.9 without; with the non-temporal loads
+        // and a 3-deep ring: 6.8 against 6.5); with pages they are left in
+        // flight (5.8 against 5.3 TB/s with plain loads): the scattered
+        // 4 KiB page reads need the overlap.
         if constexpr (!PAGED) wait_vmem_all();
         const uint32_t vbase = lds_u32(vst);
         uint32_t va[2][D / 32];
