@@ -11,8 +11,8 @@
 // gfx950 mapping:
 //   * Each wave owns RB blocks of 32 query rows.  It computes S^T = K * Q^T
 //     for 32 keys at a time with v_mfma_f32_32x32x16_bf16: one query row per
-//     lane column and 16 keys per lane, so the row maximum is in-lane plus
-//     one exchange with lane^32.  Every K fragment read from LDS feeds RB
+//     lane column and 16 keys per lane, so a row's maximum and sum are
+//     in-lane plus one exchange with lane^32.  Every K fragment read from LDS feeds RB
 //     MFMAs, and so does every V fragment: LDS read traffic per FLOP falls
 //     as 1/RB.  (At RB = 1 one 32x32x16 MFMA per SIMD per 32 clocks
 //     consumes 128 B/clock per CU of LDS reads; LDS was measured to deliver
@@ -39,12 +39,14 @@
 //     pv_tile): the compiler otherwise keeps too few reads in flight and
 //     stalls the V^T reads behind the tile prefetches.  The P V MFMAs issue
 //     at raised wave priority.
-//   * Softmax in the exp2 domain: the row maximum is taken on raw scores,
-//     one FMA forms score * scale * log2(e) - base, and the base is only
-//     moved when a row's maximum grows by more than 8 (so weights stay
-//     <= 2^8 and the O rescale is rare; the final O / l is the same for any
-//     base).  Row sums add the bf16-rounded weights with v_dot2_f32_bf16, so
-//     O stays a convex combination of V's rows.
+//   * Softmax in the exp2 domain: one FMA forms score * scale * log2(e) -
+//     base per weight.  No row maximum is taken while the weights stay
+//     small: the row sums (which are needed anyway) show when a base must
+//     move, and only then is the exact row maximum taken and the weights
+//     recomputed (so weights stay below 2^16 and the O rescale is rare; the
+//     final O / l is the same for any base).  Row sums add the bf16-rounded
+//     weights with v_dot2_f32_bf16, so O stays a convex combination of V's
+//     rows.
 //   * Causal: key tiles wholly above the diagonal are never visited (per
 //     workgroup) or skipped (per wave and row block); only tiles that cross
 //     the diagonal or the end of the keys pay for the element mask (Ch. 11
@@ -127,6 +129,9 @@ struct STile {
 // below it), and key block kb adds the immediate kb * 32 rows.  Four groups
 // ahead measured best (two: -1%, six or eight: no better).
 constexpr int kScoreReadAhead = 4;
+// Largest share of a row's weight sum one lane may hold before the row's
+// exponent base is moved (see the step below).
+constexpr float kSumGuard = 65536.f;
 template <int D, int BN, int RB, int KOFF, int I>
 __device__ __attribute__((always_inline)) inline bf16x8 score_read(uint32_t a0) {
     constexpr int NKB = BN / 32;
@@ -325,7 +330,8 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         if (!wave_live(j0)) return;
         score_tile<D, BN, RB, PAR * TILE>(s_cur, ka0, qf);
 
-        // Per row block: mask, base update.
+        // Per row block: element mask on tiles that cross the diagonal, a
+        // window edge or the end of the keys.
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             // This block's rows see none of these keys: skip.
@@ -346,26 +352,70 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                     }
                 }
             }
+        }
 
-            // This lane's maximum (16 keys of each block; the other half of
-            // the row lives in lane ^ 32).  The base only moves when some
-            // lane's maximum exceeds it by more than 8; only then are the two
-            // halves exchanged, so both lanes of a row share one base.
-            // Two independent chains of three-input maxima (v_max3_f32, two
-            // new values per instruction).
-            float mxa = -INFINITY, mxb = -INFINITY;
+        // Weights 2^(score * c - base), rounded to bf16 in place (they are
+        // the B operand of P V), and this lane's share of the row sum, taken
+        // from the rounded weights.  A row block with no visible key in this
+        // tile contributes nothing: its weights are zero.
+        bf16x8 pb[RB][BN / 16];
+        float psum[RB];
+        auto weigh = [&]() {
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
+            for (int rb = 0; rb < RB; ++rb) {
+                const bool live = j0 < rb_kv_end[rb] && j0 + BN > rb_kv_begin[rb];
+                const float m_sub = (m_use[rb] == -INFINITY) ? 0.f : m_use[rb];
+                const float cc = live ? c : 0.f;
+                const float msub = live ? m_sub : INFINITY;
+                float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-                for (int j = 0; j < 16; j += 4) {
-                    mxa = fmaxf(fmaxf(mxa, s_cur.acc[rb][kb][j]), s_cur.acc[rb][kb][j + 1]);
-                    mxb = fmaxf(fmaxf(mxb, s_cur.acc[rb][kb][j + 2]), s_cur.acc[rb][kb][j + 3]);
+                for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+                    for (int j = 0; j < 16; j += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[rb][kb][j], cc, -msub));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[rb][kb][j + 1], cc, -msub));
+                        const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                        if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
+                        else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
+                        pb[rb][kb * 2 + (j >> 3)][j & 7] = pp[0];
+                        pb[rb][kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
+                    }
                 }
+                psum[rb] = ps0 + ps1;
             }
-            const float mx = fmaxf(mxa, mxb);
-            if (__any(mx * c > m_use[rb] + 8.f)) {
+        };
+        weigh();
+
+        // The base of a row stays where it is as long as every weight is
+        // small enough: no row maximum is taken on that path.  The base moves
+        // (to the row's exact maximum, both halves of the row exchanged via
+        // lane ^ 32) only when some lane's share of a row sum exceeds 2^16
+        // (a weight grew past 2^16 / (BN / 2), or overflowed to infinity), or
+        // when a row has no base yet; the weights are then recomputed.  So
+        // weights stay below 2^16 and the fp32 accumulators far from
+        // overflow; O / l is the same for any base.
+        bool rebase = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) rebase |= (m_use[rb] == -INFINITY) || !(psum[rb] <= kSumGuard);
+        if (__any(rebase)) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                if (j0 >= rb_kv_end[rb] || j0 + BN <= rb_kv_begin[rb]) continue;
+                // This lane's maximum: two chains of three-input maxima.
+                float mxa = -INFINITY, mxb = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+                    for (int j = 0; j < 16; j += 4) {
+                        mxa = fmaxf(fmaxf(mxa, s_cur.acc[rb][kb][j]), s_cur.acc[rb][kb][j + 1]);
+                        mxb = fmaxf(fmaxf(mxb, s_cur.acc[rb][kb][j + 2]), s_cur.acc[rb][kb][j + 3]);
+                    }
+                }
+                const float mx = fmaxf(mxa, mxb);
                 const float m_row = fmaxf(mx, swap_halves(mx, xaddr)) * c;  // -inf: no visible key yet
                 const float m_t = fmaxf(m_use[rb], m_row);
+                // While a row has no base it has accumulated nothing, so
+                // alpha = 0 (or 1 when it still has no key) is exact.
                 const float alpha = (m_t == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_use[rb] - m_t);
                 l_run[rb] *= alpha;
 #pragma unroll
@@ -375,33 +425,10 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                 }
                 m_use[rb] = m_t;
             }
+            weigh();
         }
-
-        bf16x8 pb[RB][BN / 16];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            // A row block with no visible key in this tile contributes
-            // nothing: its weights are zero.
-            const bool live = j0 < rb_kv_end[rb] && j0 + BN > rb_kv_begin[rb];
-            const float m_sub = (m_use[rb] == -INFINITY) ? 0.f : m_use[rb];
-            const float cc = live ? c : 0.f;
-            const float msub = live ? m_sub : INFINITY;
-            float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-                for (int j = 0; j < 16; j += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[rb][kb][j], cc, -msub));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur.acc[rb][kb][j + 1], cc, -msub));
-                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
-                    if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
-                    else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
-                    pb[rb][kb * 2 + (j >> 3)][j & 7] = pp[0];
-                    pb[rb][kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
-                }
-            }
-            l_run[rb] += ps0 + ps1;
-        }
+        for (int rb = 0; rb < RB; ++rb) l_run[rb] += psum[rb];
 
         // O^T += V^T P^T for tile t.
         const uint32_t vbase = lds_u32(vring + PAR * TILE);
