@@ -235,6 +235,43 @@ def test_large_logits_stay_finite():
         assert G.max_err(got, want) <= G.TOL["bf16"]
 
 
+def _ramped_keys(k, direction):
+    """K with key j's row scaled by 1 + 3j/T (direction +1: scores grow along
+    the keys, so running row maxima keep jumping) or by 4 - 3j/T (direction
+    -1: early keys dominate and later weights sit far below the base);
+    rounded back to bf16."""
+    K = f64(k, "bf16")
+    T = K.shape[2]
+    j = np.arange(T, dtype=np.float64) / T
+    ramp = 1.0 + 3.0 * j if direction > 0 else 4.0 - 3.0 * j
+    return inputs.f32_to_bf16_bits((K * ramp[None, None, :, None]).astype(np.float32))
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+@pytest.mark.parametrize("B,H_q,H_kv,T,D,causal,rows", [
+    (1, 4, 2, 1100, 128, True, None),
+    (2, 4, 4, 700, 64, False, None),
+    (1, 32, 8, 4100, 128, True, list(range(0, 40)) + list(range(2000, 2040)) + list(range(4060, 4100))),
+])
+def test_exponent_base_moves_on_later_tiles(direction, B, H_q, H_kv, T, D, causal, rows):
+    """The prefill kernels keep a row's exponent base until the weights grow
+    too large and then move it to the exact row maximum; growing scores make
+    that happen on many later tiles (both launch shapes: the last case uses
+    the 8-wave one)."""
+    seed = 671 + T + D + direction
+    q = gen(seed, (B, H_q, T, D), "bf16")
+    k = _ramped_keys(gen(seed + 1, (B, H_kv, T, D), "bf16"), direction)
+    v = gen(seed + 2, (B, H_kv, T, D), "bf16")
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    got = G.prefill(q, k, v, causal, scale, "bf16")
+    assert np.all(np.isfinite(got))
+    want = oracle.attention(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), scale, causal, rows=rows)
+    if rows is not None:
+        got = got[:, :, rows]
+    err = G.max_err(got, want)
+    assert err <= G.TOL["bf16"], f"max|dO| {err:.3e}"
+
+
 # --- the check has teeth: the pages' pitfalls must fail it -----------------------------
 def test_negative_controls_exceed_tolerance():
     w = BY_ORDINAL[2]
