@@ -63,9 +63,15 @@ qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16*
     const int mt = blockIdx.x / n_nt, nt = blockIdx.x - mt * n_nt;
     const int m0 = mt * kTM, n0 = nt * kTN;
 
+    // The row counts are wave-uniform, but the clamp compiles to a vector
+    // instruction; readfirstlane keeps the buffer resources in scalar
+    // registers (otherwise every tile load is wrapped in a loop over
+    // distinct resource values).
     const uint32_t rowb = (uint32_t)d_model * 2;
-    const auto rX = make_rsrc(X + (size_t)m0 * d_model, (uint32_t)max(0, min(kTM, M - m0)) * rowb);
-    const auto rW = make_rsrc(W + (size_t)n0 * d_model, (uint32_t)max(0, min(kTN, N - n0)) * rowb);
+    const int x_rows = __builtin_amdgcn_readfirstlane(max(0, min(kTM, M - m0)));
+    const int w_rows = __builtin_amdgcn_readfirstlane(max(0, min(kTN, N - n0)));
+    const auto rX = make_rsrc(X + (size_t)m0 * d_model, (uint32_t)x_rows * rowb);
+    const auto rW = make_rsrc(W + (size_t)n0 * d_model, (uint32_t)w_rows * rowb);
 
     // One k tile of X (256 rows) and of W (256 rows): 32 + 32 loads of
     // 1 KiB, 4 + 4 per wave.
