@@ -27,13 +27,24 @@
 //   * 64-wide k tiles of X and W go HBM -> LDS with 16-byte buffer loads that
 //     write LDS directly, double buffered; 128-byte rows use the same XOR
 //     swizzle of 16-byte chunks as the attention kernels' K tiles (conflict-
-//     free ds_read_b128 operand reads).
+//     free ds_read_b128 operand reads).  The fragments of the next k step
+//     are read while the current step's MFMAs run.
 //   * Tokens past B T and features past N read as zero (range-checked buffer
 //     resources) and are not stored.  d_model must be a multiple of 64.
 #include "kernel_common.h"
 
 namespace attn {
 namespace {
+
+// s_waitcnt lgkmcnt(N) that also redefines the six fragments g, so no use
+// of them can be scheduled before it (LDS reads complete in issue order).
+template <int N>
+__device__ inline void lds_wait_bind6(bf16x8 (&g)[6]) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(g[0]), "+v"(g[1]), "+v"(g[2]), "+v"(g[3]), "+v"(g[4]), "+v"(g[5])
+                 : "n"(N));
+}
 
 constexpr int kWaves = 8;
 constexpr int kTM = 256;   // tokens per workgroup
@@ -74,10 +85,12 @@ qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16*
     const auto rW = make_rsrc(W + (size_t)n0 * d_model, (uint32_t)w_rows * rowb);
 
     // One k tile of X (256 rows) and of W (256 rows): 32 + 32 loads of
-    // 1 KiB, 4 + 4 per wave.
+    // 1 KiB, 4 + 4 per wave.  LDS holds the X tiles of both stages, then
+    // the W tiles of both stages, so every operand read's stage and block
+    // offset fits the 16-bit immediate of ds_read_b128.
     auto issue = [&](int kt, int buf) {
-        unsigned char* xs = smem + buf * kStage;
-        unsigned char* ws = xs + kXTile;
+        unsigned char* xs = smem + buf * kXTile;
+        unsigned char* ws = smem + 2 * kXTile + buf * kWTile;
         const uint32_t kb = (uint32_t)kt * kRowB;
 #pragma unroll
         for (int n = 0; n < kXTile / (1024 * kWaves); ++n) {
@@ -99,35 +112,68 @@ qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16*
 
     const int n_kt = d_model / kTK;
     issue(0, 0);
-    // Lane offsets of the operand fragments within a tile: row l32 of the
-    // wave's block, chunk 2s + hi for k step s.
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int buf = kt & 1;
+    // Operand fragments: lane (row l32 of a 32-row block, half hi) reads
+    // the 16-byte chunk 2s + hi of its row for k step s, stored at chunk
+    // (2s + hi) ^ swz(row).  swz depends on the row's low 4 bits only, so
+    // every block of the wave shares the lane's chunk, and step s flips
+    // bits 5-6 of the step-0 address: address = a0 ^ 32s, plus immediates
+    // for the stage and the 32-row block.
+    const uint32_t c0 = (uint32_t)((hi ^ swz<kCPR>(l32)) * 16);
+    const uint32_t xa0 = lds_u32(smem) + (uint32_t)((wt * 64 + l32) * kRowB) + c0;
+    const uint32_t wa0 = lds_u32(smem) + 2 * kXTile + (uint32_t)((wf * 128 + l32) * kRowB) + c0;
+    uint32_t xa[kTK / 16], wa[kTK / 16];
+#pragma unroll
+    for (int st = 0; st < kTK / 16; ++st) {
+        xa[st] = xa0 ^ (uint32_t)(32 * st);
+        wa[st] = wa0 ^ (uint32_t)(32 * st);
+    }
+    // The fragments of k step s + 1 are read (inline assembly, waits bound
+    // to the fragment registers) while the 8 MFMAs of step s run; the
+    // compiler's own reads were issued only a few MFMAs ahead.
+    auto tile = [&](int kt, auto stage) {
+        constexpr int B = decltype(stage)::value;
         wait_vmem_all();
-        __syncthreads();  // tile kt landed for every wave; tile kt-1's buffer is free
-        if (kt + 1 < n_kt) issue(kt + 1, buf ^ 1);
-        const unsigned char* xs = smem + buf * kStage;
-        const unsigned char* ws = xs + kXTile;
-#pragma unroll
-        for (int s = 0; s < kTK / 16; ++s) {
-            bf16x8 xf[2], wfr[4];
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const int row = wt * 64 + tb * 32 + l32;
-                xf[tb] = *reinterpret_cast<const bf16x8*>(xs + row * kRowB + (((2 * s + hi) ^ swz<kCPR>(row)) * 16));
-            }
+        __syncthreads();  // tile kt landed for every wave; the other stage is free
+        if (kt + 1 < n_kt) issue(kt + 1, B ^ 1);
+        bf16x8 f[2][6];  // [ring slot][X block 0, 1, W block 0..3]
+        auto read = [&](bf16x8 (&g)[6], auto step) {
+            constexpr int S = decltype(step)::value;
+            g[0] = ds_read_b128_asm<B * kXTile>(xa[S]);
+            g[1] = ds_read_b128_asm<B * kXTile + 32 * kRowB>(xa[S]);
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb) {
-                const int row = wf * 128 + fb * 32 + l32;
-                wfr[fb] = *reinterpret_cast<const bf16x8*>(ws + row * kRowB + (((2 * s + hi) ^ swz<kCPR>(row)) * 16));
+                switch (fb) {
+                    case 0: g[2] = ds_read_b128_asm<B * kWTile>(wa[S]); break;
+                    case 1: g[3] = ds_read_b128_asm<B * kWTile + 32 * kRowB>(wa[S]); break;
+                    case 2: g[4] = ds_read_b128_asm<B * kWTile + 64 * kRowB>(wa[S]); break;
+                    default: g[5] = ds_read_b128_asm<B * kWTile + 96 * kRowB>(wa[S]); break;
+                }
             }
+        };
+        auto mma = [&](bf16x8 (&g)[6]) {
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb) {
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
-                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wfr[fb], xf[tb], acc[fb][tb], 0, 0, 0);
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g[2 + fb], g[tb], acc[fb][tb], 0, 0, 0);
             }
-        }
+        };
+        read(f[0], std::integral_constant<int, 0>{});
+        read(f[1], std::integral_constant<int, 1>{});
+        lds_wait_bind6<6>(f[0]);
+        mma(f[0]);
+        read(f[0], std::integral_constant<int, 2>{});
+        lds_wait_bind6<6>(f[1]);
+        mma(f[1]);
+        read(f[1], std::integral_constant<int, 3>{});
+        lds_wait_bind6<6>(f[0]);
+        mma(f[0]);
+        lds_wait_bind6<0>(f[1]);
+        mma(f[1]);
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < n_kt) tile(kt + 1, std::integral_constant<int, 1>{});
     }
 
     // Epilogue: lane (token column l32, half hi) holds features
