@@ -68,6 +68,7 @@ CASES = [
     (3, 77, 768, 12, 12, 64),
     (1, 1000, 4096, 32, 8, 128),
     (2, 300, 512, 4, 1, 128),
+    (1, 70, 192, 3, 1, 64),        # N = 320: ragged feature tile; 3 k tiles (odd)
 ]
 
 
