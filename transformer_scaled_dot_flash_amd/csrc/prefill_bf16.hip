@@ -322,13 +322,25 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         // V(t-1), whose slots are refilled below.
         wait_vmem_all();
         __syncthreads();
-        if (t + 1 < n_kt) {
-            issue_k(t + 1);
-            issue_v(t + 1);
-        }
+        // The next tile's loads go out right after the barrier with 64-key
+        // tiles (short steps need the lead), after this tile's score MFMAs
+        // with 128-key tiles (measured +0.6-0.8% there, -1.5-2% with 64-key
+        // tiles).
+        constexpr bool kIssueAfterScores = BN >= 128;
+        auto issue_next = [&]() {
+            if (t + 1 < n_kt) {
+                issue_k(t + 1);
+                issue_v(t + 1);
+            }
+        };
+        if (!kIssueAfterScores) issue_next();
         // Tiles above the diagonal or left of this wave's window: nothing to do.
-        if (!wave_live(j0)) return;
+        if (!wave_live(j0)) {
+            if (kIssueAfterScores) issue_next();
+            return;
+        }
         score_tile<D, BN, RB, PAR * TILE>(s_cur, ka0, qf);
+        if (kIssueAfterScores) issue_next();
 
         // Per row block: element mask on tiles that cross the diagonal, a
         // window edge or the end of the keys.
