@@ -102,7 +102,7 @@ def cpu_baseline(budget_s=15.0):
 
 KERNELS = {
     # name in profiles/ : (mangled kernel-name substring, source files)
-    # prefill<D=128, causal, contiguous, RB=1, BN=64, 8 waves>; decode<D=128, contiguous / paged>
+    # prefill<D=128, causal, contiguous, RB=1, BN=128, 8 waves>; decode<D=128, contiguous / paged>
     "prefill_bf16_T8192_D128_gqa": ("prefill_bf16_kernelILi128ELb1ELb0ELi1ELi128ELi8E",
                                     ["prefill_bf16.hip", "kernel_common.h"]),
     "decode_bf16_B64_T4096_D128": ("decode_split_kernelILi128ELb0E", ["decode_bf16.hip", "kernel_common.h"]),
