@@ -55,6 +55,7 @@ constexpr int kCPR = kRowB / 16;               // 16-byte chunks per row (8)
 constexpr int kXTile = kTM * kRowB;            // 32 KiB
 constexpr int kWTile = kTN * kRowB;            // 32 KiB
 constexpr int kStage = kXTile + kWTile;
+constexpr int kGroupM = 8;  // token tiles per group of the tile order
 
 template <int D>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void
@@ -71,7 +72,21 @@ qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16*
     const int wt = wave & 3;   // token block of 64
     const int wf = wave >> 2;  // feature block of 128
 
-    const int mt = blockIdx.x / n_nt, nt = blockIdx.x - mt * n_nt;
+    // Workgroup id -> output tile.  Dispatch sends id to XCD (id mod 8).
+    // Each XCD takes a contiguous range of tiles in grouped order (kGroupM
+    // token tiles per group, feature tiles walking within the group), i.e.
+    // a compact block of rows and columns, so the X and W tiles it reads
+    // are shared through its own L2; the plain row-major order gave every
+    // XCD every token tile.
+    const int n_tiles = (int)gridDim.x;
+    int v = (int)blockIdx.x;
+    if ((n_tiles & 7) == 0) v = (v & 7) * (n_tiles >> 3) + (v >> 3);
+    const int n_mt = n_tiles / n_nt;
+    const int group = v / (kGroupM * n_nt);
+    const int first_m = group * kGroupM;
+    const int gsize = min(n_mt - first_m, kGroupM);
+    const int in_group = v - group * kGroupM * n_nt;
+    const int mt = first_m + in_group % gsize, nt = in_group / gsize;
     const int m0 = mt * kTM, n0 = nt * kTN;
 
     // The row counts are wave-uniform, but the clamp compiles to a vector
