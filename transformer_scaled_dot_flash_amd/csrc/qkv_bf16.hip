@@ -29,6 +29,8 @@
 //     swizzle of 16-byte chunks as the attention kernels' K tiles (conflict-
 //     free ds_read_b128 operand reads).  The fragments of the next k step
 //     are read while the current step's MFMAs run.
+//   * Each XCD takes a compact block of output tiles (grouped tile order),
+//     so the X and W tiles it reads are shared through its own L2.
 //   * Tokens past B T and features past N read as zero (range-checked buffer
 //     resources) and are not stored.  d_model must be a multiple of 64.
 #include "kernel_common.h"
