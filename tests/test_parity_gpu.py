@@ -314,7 +314,8 @@ def test_empty_problems_are_noops():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("D,causal,H_q,H_kv,B", [(128, True, 64, 8, 1), (64, False, 32, 32, 2)])
+@pytest.mark.parametrize("D,causal,H_q,H_kv,B", [(128, True, 64, 8, 1), (64, False, 32, 32, 2),
+                                                  (64, True, 36, 3, 1)])  # 3 kv units: no XCD grouping
 def test_large_problem_configuration_sampled(D, causal, H_q, H_kv, B):
     """Shapes big enough for the 8-wave prefill configuration (T >= 4096 and
     at least 512 workgroups of 256 rows), ragged T."""
