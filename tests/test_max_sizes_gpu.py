@@ -1,0 +1,124 @@
+"""Largest slices the C ABI accepts: one (batch, head) slice of Q and O, or of
+K and V, just under 2 GiB (the kernels address a slice with 32-bit offsets
+from a range-checked buffer resource, and the host rejects anything larger).
+
+Running the oracle over eight million keys is out of reach on the CPU, so the
+inputs are periodic: K and V (or Q) repeat a seeded block of 256 rows.  Each
+key of the block then occurs n times with the same score, its weight is n
+times larger, and the softmax-weighted mean over all keys equals the one over
+a single block: the oracle on 256 keys.  Likewise an output row depends only
+on its query row, so repeated query rows must give repeated output rows."""
+import math
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+import oracle
+from transformer_scaled_dot_flash_amd import attn as abi
+from transformer_scaled_dot_flash_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+P = 256                                        # rows per repeated block
+T_MAX = (2 ** 31 // (D * 2)) // P * P - P      # 8388352 rows: a slice of 2 GiB - 64 KiB
+SCALE = float(np.float32(1.0 / math.sqrt(D)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    abi.load_library()  # raises when the HIP library is missing: no fallback
+
+
+def _f64(bits):
+    return inputs.as_f64(bits, "bf16")
+
+
+def _guards_intact(buf):
+    """The sentinel bands around O (read back alone: O itself may be 2 GiB)."""
+    s = G.SENTINEL["bf16"]
+    head = buf[:G.GUARD].cpu().numpy().view(np.uint16)
+    tail = buf[-G.GUARD:].cpu().numpy().view(np.uint16)
+    return bool(np.all(head == s) and np.all(tail == s))
+
+
+def test_prefill_kv_slice_just_under_2GiB():
+    torch = G.torch_mod()
+    assert T_MAX * D * 2 < 2 ** 31 and (T_MAX + P) * D * 2 >= 2 ** 31 - 2 ** 16
+    T_q, H_q = 200, 2
+    q = inputs.normal(901, (1, H_q, T_q, D), "bf16")
+    kb = inputs.normal(902, (1, 1, P, D), "bf16")
+    vb = inputs.normal(903, (1, 1, P, D), "bf16")
+    want = oracle.attention(_f64(q), _f64(kb), _f64(vb), SCALE, False)
+    qd = G.to_device(q, "bf16")
+    kd = G.to_device(kb, "bf16").repeat(1, 1, T_MAX // P, 1)
+    vd = G.to_device(vb, "bf16").repeat(1, 1, T_MAX // P, 1)
+    buf, o = G.guarded_output((1, H_q, T_q, D), "bf16")
+    G.note(f"attn_fwd_prefill B=1 H_q={H_q} H_kv=1 T_q={T_q} T_kv={T_MAX} D={D} causal=0 (max K/V slice)")
+    abi.attn_fwd_prefill(qd, kd, vd, o, 1, H_q, 1, T_q, T_MAX, D, False, SCALE, abi.ATTN_BF16,
+                         torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert _guards_intact(buf), "write outside O"
+    got = G.to_f64(o, "bf16")
+    del kd, vd
+    torch.cuda.empty_cache()
+    assert G.max_err(got, want) <= G.TOL["bf16"]
+
+
+def test_prefill_q_slice_just_under_2GiB():
+    torch = G.torch_mod()
+    qb = inputs.normal(911, (1, 1, P, D), "bf16")
+    k = inputs.normal(912, (1, 1, P, D), "bf16")
+    v = inputs.normal(913, (1, 1, P, D), "bf16")
+    want = oracle.attention(_f64(qb), _f64(k), _f64(v), SCALE, False)[0, 0]  # [P][D]
+    qd = G.to_device(qb, "bf16").repeat(1, 1, T_MAX // P, 1)
+    kd, vd = G.to_device(k, "bf16"), G.to_device(v, "bf16")
+    buf, o = G.guarded_output((1, 1, T_MAX, D), "bf16")
+    G.note(f"attn_fwd_prefill B=1 H_q=1 H_kv=1 T_q={T_MAX} T_kv={P} D={D} causal=0 (max Q/O slice)")
+    abi.attn_fwd_prefill(qd, kd, vd, o, 1, 1, 1, T_MAX, P, D, False, SCALE, abi.ATTN_BF16,
+                         torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert _guards_intact(buf), "write outside O"
+    rows = np.r_[0:P, T_MAX // 2 - 3:T_MAX // 2 + 3, T_MAX - P:T_MAX]
+    got = G.to_f64(o[0, 0, torch.as_tensor(rows, device="cuda")], "bf16")
+    del qd, buf, o
+    torch.cuda.empty_cache()
+    assert G.max_err(got, want[rows % P]) <= G.TOL["bf16"]
+
+
+def test_decode_kv_slice_just_under_2GiB():
+    torch = G.torch_mod()
+    H_q = 8
+    q = inputs.normal(921, (1, H_q, 1, D), "bf16")
+    kb = inputs.normal(922, (1, 1, P, D), "bf16")
+    vb = inputs.normal(923, (1, 1, P, D), "bf16")
+    want = oracle.attention(_f64(q), _f64(kb), _f64(vb), SCALE, False)
+    qd = G.to_device(q, "bf16")
+    kd = G.to_device(kb, "bf16").repeat(1, 1, T_MAX // P, 1)
+    vd = G.to_device(vb, "bf16").repeat(1, 1, T_MAX // P, 1)
+    buf, o = G.guarded_output((1, H_q, 1, D), "bf16")
+    nbytes = abi.attn_fwd_decode_workspace_bytes(1, H_q, 1, T_MAX, D, abi.ATTN_BF16, 0)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    G.note(f"attn_fwd_decode B=1 H_q={H_q} H_kv=1 T_kv={T_MAX} D={D} (max K/V slice)")
+    abi.attn_fwd_decode(qd, kd, vd, o, 1, H_q, 1, 1, T_MAX, D, False, SCALE, abi.ATTN_BF16, 0, ws, nbytes,
+                        torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert _guards_intact(buf), "write outside O"
+    got = G.to_f64(o, "bf16")
+    del kd, vd
+    torch.cuda.empty_cache()
+    assert G.max_err(got, want) <= G.TOL["bf16"]
+
+
+def test_one_row_more_is_rejected():
+    """The host rejects a slice of 2 GiB or more before any launch."""
+    torch = G.torch_mod()
+    big = (2 ** 31) // (D * 2)  # exactly 2 GiB per slice
+    q = torch.empty((1, 1, 8, D), dtype=torch.bfloat16, device="cuda")
+    st = abi.attn_fwd_prefill(q, q, q, q.clone(), 1, 1, 1, 8, big, D, False, SCALE, abi.ATTN_BF16,
+                              torch.cuda.current_stream(), check=False)
+    assert abi.STATUS_NAMES[st] == "ATTN_ERR_INVALID_SHAPE"
