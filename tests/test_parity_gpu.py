@@ -339,3 +339,29 @@ def test_long_sequence_sampled():
     rows = [0, 1, 127, 128, 16383, 16384, 32640, 32767]
     want = oracle.attention(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), 0.088, True, rows=rows)
     assert G.max_err(got[:, :, rows], want) <= G.TOL["bf16"]
+
+
+def test_library_loaded_before_torch_in_a_fresh_process():
+    """Loading the library before torch must not leave the process with two
+    HIP runtimes (torch bundles its own): a prefill in a fresh interpreter
+    whose first act is load_library() matches the oracle."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parent.parent
+    code = (
+        "import sys; sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+        "from transformer_scaled_dot_flash_amd import attn as abi\n"
+        "abi.load_library()\n"
+        "import numpy as np, gpu_util as G, oracle\n"
+        "from transformer_scaled_dot_flash_amd import inputs\n"
+        "q = inputs.normal(961, (1, 2, 70, 64), 'bf16'); k = inputs.normal(962, (1, 1, 90, 64), 'bf16')\n"
+        "v = inputs.normal(963, (1, 1, 90, 64), 'bf16')\n"
+        "got = G.prefill(q, k, v, True, 0.125, 'bf16')\n"
+        "f = lambda x: inputs.as_f64(x, 'bf16')\n"
+        "err = G.max_err(got, oracle.attention(f(q), f(k), f(v), 0.125, True))\n"
+        "assert err <= G.TOL['bf16'], err\n"
+        "print('ok', err)\n"
+    ) % (str(root), str(root / "tests"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]

@@ -71,6 +71,15 @@ def load_library(path: Path | str | None = None):
     if not p.exists():
         raise RuntimeError(f"HIP attention library not built: {p} is missing "
                            "(run __graft_entry__.build())")
+    # PyTorch ships its own HIP runtime under the same soname.  Loaded first,
+    # it is the runtime this library binds to; loaded after this library,
+    # torch would bring a second runtime into the process, whose device and
+    # stream state this library cannot see (launches then fail with
+    # hipErrorNoDevice).  So torch, when installed, is loaded before it.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(str(p))
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
