@@ -1,0 +1,151 @@
+"""Seeded random shapes through every attention entry point, each compared
+with the oracle at the contract's tolerance: batch and head counts
+(MHA, GQA with groups of 1-40, MQA), ragged lengths of 1-700 rows, D = 64 and
+128, causal or not, scales 1/sqrt(D), -1/sqrt(D), 0 and 2/sqrt(D), fp32 and
+bf16
+windows of 1 key up to wider than the keys
+packed batches with empty
+sequences
+decode split counts
+paged caches with empty sequences and page
+sizes 16-128.  The cases are fixed by the seed, so a failure names a
+reproducible case."""
+import math
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+import oracle
+import test_paged_gpu as PG
+import test_window_varlen_gpu as W
+from transformer_scaled_dot_flash_amd import attn as abi
+from transformer_scaled_dot_flash_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SEED = 20261202
+N = 60  # dense prefill cases (the other kinds get N // 3 or N // 2)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    abi.load_library()
+
+
+def f64(x, dt="bf16"):
+    return inputs.as_f64(x, dt)
+
+
+def _sweep(kind):
+    rng = np.random.default_rng([SEED, ["prefill", "window", "varlen", "decode", "paged"].index(kind)])
+    fails = []
+
+    def report(kind_, case, err, tol):
+        print(f"{kind_} {case} err={err:.3e}")
+        if not err <= tol:
+            fails.append((case, err))
+
+    def pick_heads():
+        H_kv = int(rng.choice([1, 2, 3, 4]))
+        Gq = int(rng.choice([1, 2, 3, 4, 8]))
+        return H_kv * Gq, H_kv
+
+    if kind == 'prefill':
+        for i in range(N):  # dense prefill
+            B = int(rng.integers(1, 4))
+            H_q, H_kv = pick_heads()
+            D = int(rng.choice([64, 128]))
+            dtype = "f32" if rng.random() < 0.2 else "bf16"
+            causal = bool(rng.random() < 0.6)
+            T_q = int(rng.integers(1, 600))
+            T_kv = int(rng.integers(T_q if causal else 1, 700))
+            sc = [1 / math.sqrt(D), -1 / math.sqrt(D), 0.0, 2.0 / math.sqrt(D)][int(rng.choice(4, p=[0.7, 0.1, 0.1, 0.1]))]
+            scale = float(np.float32(sc))
+            s = int(rng.integers(1 << 30))
+            q = inputs.normal(s, (B, H_q, T_q, D), dtype)
+            k = inputs.normal(s + 1, (B, H_kv, T_kv, D), dtype)
+            v = inputs.normal(s + 2, (B, H_kv, T_kv, D), dtype)
+            got = G.prefill(q, k, v, causal, scale, dtype)
+            want = oracle.attention(f64(q, dtype), f64(k, dtype), f64(v, dtype), scale, causal)
+            report("prefill", (B, H_q, H_kv, T_q, T_kv, D, causal, dtype, round(scale, 4)), G.max_err(got, want), G.TOL[dtype])
+    if kind == 'window':
+        for i in range(N // 3):  # window
+            B = int(rng.integers(1, 3))
+            H_q, H_kv = pick_heads()
+            D = int(rng.choice([64, 128]))
+            T_q = int(rng.integers(1, 600))
+            T_kv = int(rng.integers(T_q, 700))
+            Wn = int(rng.integers(1, T_kv + 6))
+            s = int(rng.integers(1 << 30))
+            scale = float(np.float32(1 / math.sqrt(D)))
+            q = inputs.normal(s, (B, H_q, T_q, D), "bf16")
+            k = inputs.normal(s + 1, (B, H_kv, T_kv, D), "bf16")
+            v = inputs.normal(s + 2, (B, H_kv, T_kv, D), "bf16")
+            got = W.run_window(q, k, v, Wn, scale)
+            want = oracle.attention(f64(q), f64(k), f64(v), scale, True, window=Wn)
+            report("window", (B, H_q, H_kv, T_q, T_kv, D, Wn), G.max_err(got, want), G.TOL["bf16"])
+    if kind == 'varlen':
+        for i in range(N // 3):  # varlen
+            Bq = int(rng.integers(1, 6))
+            H_q, H_kv = pick_heads()
+            D = int(rng.choice([64, 128]))
+            causal = bool(rng.random() < 0.6)
+            Wn = int(rng.integers(1, 300)) if (causal and rng.random() < 0.3) else 0
+            lq = rng.integers(0, 400, Bq)
+            lk = np.array([int(rng.integers(max(a, 1) if causal else 1, 500)) for a in lq])
+            cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+            cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+            if cu_q[-1] == 0:
+                continue
+            s = int(rng.integers(1 << 30))
+            scale = float(np.float32(1 / math.sqrt(D)))
+            q = inputs.normal(s, (int(cu_q[-1]), H_q, D), "bf16")
+            k = inputs.normal(s + 1, (int(cu_k[-1]), H_kv, D), "bf16")
+            v = inputs.normal(s + 2, (int(cu_k[-1]), H_kv, D), "bf16")
+            got = W.run_varlen(q, k, v, cu_q, cu_k, causal, Wn, scale)
+            want = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_q, cu_k, scale, causal, window=Wn)
+            report("varlen", (list(lq), list(lk), H_q, H_kv, D, causal, Wn), G.max_err(got, want), G.TOL["bf16"])
+    if kind == 'decode':
+        for i in range(N // 2):  # decode
+            B = int(rng.integers(1, 9))
+            H_kv = int(rng.integers(1, 9))
+            Gq = int(rng.choice([1, 2, 4, 5, 8, 16, 32, 40]))
+            H_q = H_kv * Gq
+            D = int(rng.choice([64, 128]))
+            T_kv = int(rng.integers(1, 3000))
+            splits = int(rng.choice([0, 0, 1, 2, 3, 7, 16]))
+            dtype = "f32" if rng.random() < 0.15 else "bf16"
+            s = int(rng.integers(1 << 30))
+            scale = float(np.float32(1 / math.sqrt(D)))
+            q = inputs.normal(s, (B, H_q, 1, D), dtype)
+            k = inputs.normal(s + 1, (B, H_kv, T_kv, D), dtype)
+            v = inputs.normal(s + 2, (B, H_kv, T_kv, D), dtype)
+            got = G.decode(q, k, v, scale, dtype, splits)
+            want = oracle.attention(f64(q, dtype), f64(k, dtype), f64(v, dtype), scale, False)
+            report("decode", (B, H_q, H_kv, T_kv, D, splits, dtype), G.max_err(got, want), G.TOL[dtype])
+    if kind == 'paged':
+        for i in range(N // 3):  # paged decode
+            B = int(rng.integers(1, 6))
+            H_kv = int(rng.integers(1, 5))
+            Gq = int(rng.choice([1, 2, 4, 8, 16]))
+            H_q = H_kv * Gq
+            D = int(rng.choice([64, 128]))
+            ps = int(rng.choice([16, 32, 64, 128]))
+            lens = [int(x) for x in rng.integers(0, 2500, B)]
+            splits = int(rng.choice([0, 0, 1, 2, 5]))
+            q, kp, vp, table, L = PG.make_case(B, H_q, H_kv, D, ps, lens, seed=int(rng.integers(1 << 20)))
+            scale = float(np.float32(1 / math.sqrt(D)))
+            got = PG.run_paged(q, kp, vp, table, L, scale, splits)
+            want = PG.oracle_paged(q, kp, vp, table, L, scale)
+            report("paged", (B, H_q, H_kv, D, ps, lens, splits), G.max_err(got, want), G.TOL["bf16"])
+    return fails
+
+
+@pytest.mark.parametrize("kind", ["prefill", "window", "varlen", "decode", "paged"])
+def test_random_shapes_match_oracle(kind):
+    fails = _sweep(kind)
+    assert not fails, f"{len(fails)} {kind} cases over tolerance, first: {fails[:3]}"
