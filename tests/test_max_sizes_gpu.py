@@ -122,3 +122,48 @@ def test_one_row_more_is_rejected():
     st = abi.attn_fwd_prefill(q, q, q, q.clone(), 1, 1, 1, 8, big, D, False, SCALE, abi.ATTN_BF16,
                               torch.cuda.current_stream(), check=False)
     assert abi.STATUS_NAMES[st] == "ATTN_ERR_INVALID_SHAPE"
+
+
+def test_paged_pool_beyond_4GiB():
+    """A paged cache whose pools (K and V) are 5 GiB each, with the pages of
+    the sequences scattered past the 2 GiB and 4 GiB marks: page bases are
+    64-bit.  Only the referenced pages are filled; the oracle sees the same
+    pages compacted into a small pool."""
+    import oracle.paged_fp64 as PO
+    torch = G.torch_mod()
+    B, H_q, H_kv, ps = 2, 8, 2, 16
+    page_bytes = H_kv * ps * D * 2
+    n_pages = (5 << 30) // page_bytes
+    lens = [300, 1000]
+    max_pages = -(-max(lens) // ps)
+    rng = np.random.default_rng(931)
+    marks = [0, (2 << 30) // page_bytes - 3, (4 << 30) // page_bytes - 5, n_pages - max_pages * B]
+    ids = np.unique(np.concatenate([m + np.arange(max_pages * B // 2) for m in marks]))
+    ids = rng.permutation(ids)[:max_pages * B]
+    table = ids.reshape(B, max_pages).astype(np.int32)
+    assert int(table.max()) < n_pages and int(table.max()) * page_bytes >= (4 << 30)
+    q = inputs.normal(932, (B, H_q, D), "bf16")
+    kp = inputs.normal(933, (ids.size, H_kv, ps, D), "bf16")  # contents of the used pages, in `ids` order
+    vp = inputs.normal(934, (ids.size, H_kv, ps, D), "bf16")
+    k_pool = torch.empty((n_pages, H_kv, ps, D), dtype=torch.bfloat16, device="cuda")
+    v_pool = torch.empty_like(k_pool)
+    where = torch.as_tensor(ids, dtype=torch.int64, device="cuda")
+    k_pool[where] = G.to_device(kp, "bf16")
+    v_pool[where] = G.to_device(vp, "bf16")
+    qd = G.to_device(q, "bf16")
+    td = torch.from_numpy(table).cuda()
+    ld = torch.as_tensor(lens, dtype=torch.int32, device="cuda")
+    buf, o = G.guarded_output((B, H_q, D), "bf16")
+    nbytes = abi.attn_fwd_decode_paged_workspace_bytes(B, H_q, H_kv, D, ps, max_pages, 0)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    G.note(f"attn_fwd_decode_paged B={B} H_q={H_q} H_kv={H_kv} D={D} page={ps} pages={n_pages} (5 GiB pools)")
+    abi.attn_fwd_decode_paged(qd, k_pool, v_pool, o, td, ld, B, H_q, H_kv, D, ps, n_pages, max_pages, SCALE,
+                              abi.ATTN_BF16, 0, ws, nbytes, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert _guards_intact(buf), "write outside O"
+    got = G.to_f64(o, "bf16")
+    del k_pool, v_pool
+    torch.cuda.empty_cache()
+    compact = np.arange(ids.size, dtype=np.int32).reshape(B, max_pages)  # table over the compacted pool
+    want = PO.decode_paged(_f64(q), _f64(kp), _f64(vp), compact, np.asarray(lens, np.int32), SCALE)
+    assert G.max_err(got, want) <= G.TOL["bf16"]
