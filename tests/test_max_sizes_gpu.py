@@ -167,3 +167,71 @@ def test_paged_pool_beyond_4GiB():
     compact = np.arange(ids.size, dtype=np.int32).reshape(B, max_pages)  # table over the compacted pool
     want = PO.decode_paged(_f64(q), _f64(kp), _f64(vp), compact, np.asarray(lens, np.int32), SCALE)
     assert G.max_err(got, want) <= G.TOL["bf16"]
+
+
+def _run_varlen(qd, kd, vd, cu_q, cu_k, H_q, H_kv, causal):
+    torch = G.torch_mod()
+    lq, lk = np.diff(cu_q), np.diff(cu_k)
+    total_q, total_k = int(cu_q[-1]), int(cu_k[-1])
+    cq = torch.as_tensor(np.asarray(cu_q, np.int32), device="cuda")
+    ck = torch.as_tensor(np.asarray(cu_k, np.int32), device="cuda")
+    buf, o = G.guarded_output((total_q, H_q, D), "bf16")
+    G.note(f"attn_fwd_prefill_varlen B={len(lq)} H_q={H_q} H_kv={H_kv} D={D} total_q={total_q} "
+           f"total_k={total_k} causal={int(causal)} (packed buffers over 4 GiB)")
+    abi.attn_fwd_prefill_varlen(qd, kd, vd, o, cq, ck, len(lq), H_q, H_kv, D, total_q, total_k,
+                                int(lq.max()), int(lk.max()), causal, 0, SCALE, abi.ATTN_BF16,
+                                torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert _guards_intact(buf), "write outside O"
+    return buf, o
+
+
+def test_varlen_packed_q_beyond_4GiB():
+    """Three sequences of 199,936 query rows each (Q and O 4.6 GiB, the last
+    sequence starting past 4 GiB) against 256 keys each; every sequence's
+    queries repeat a seeded 256-row block, so its output rows repeat the
+    oracle's rows for that block."""
+    torch = G.torch_mod()
+    H_q, H_kv, L = 32, 8, 781 * P
+    assert (L + 256) * H_q * D * 2 < 2 ** 31 and 3 * L * H_q * D * 2 > (4 << 30)
+    cu_q = np.array([0, L, 2 * L, 3 * L])
+    cu_k = np.array([0, P, 2 * P, 3 * P])
+    qb = inputs.normal(941, (3, P, H_q, D), "bf16")
+    k = inputs.normal(942, (3 * P, H_kv, D), "bf16")
+    v = inputs.normal(943, (3 * P, H_kv, D), "bf16")
+    qd = G.to_device(qb, "bf16").repeat(1, L // P, 1, 1).reshape(3 * L, H_q, D)
+    buf, o = _run_varlen(qd, G.to_device(k, "bf16"), G.to_device(v, "bf16"), cu_q, cu_k, H_q, H_kv, False)
+    rows = np.r_[0:8, L - 8:L + 8, 2 * L:2 * L + 8, 3 * L - P:3 * L]
+    got = G.to_f64(o[torch.as_tensor(rows, device="cuda")], "bf16")
+    del qd, buf, o
+    torch.cuda.empty_cache()
+    for s in range(3):
+        want = oracle.attention_varlen(_f64(qb[s]), _f64(k[s * P:(s + 1) * P]), _f64(v[s * P:(s + 1) * P]),
+                                       [0, P], [0, P], SCALE, False)
+        sel = (rows >= s * L) & (rows < (s + 1) * L)
+        assert G.max_err(got[sel], want[(rows[sel] - s * L) % P]) <= G.TOL["bf16"]
+
+
+def test_varlen_packed_kv_beyond_4GiB():
+    """Three sequences of 100 queries against 819,200 keys each (K and V
+    4.7 GiB, the last sequence's keys past 4 GiB); every sequence's keys and
+    values repeat a seeded 256-key block, so its output equals the oracle's
+    over that block."""
+    torch = G.torch_mod()
+    H_q, H_kv, Lq, L = 8, 8, 100, 3200 * P
+    assert (L + 64) * H_kv * D * 2 < 2 ** 31 and 3 * L * H_kv * D * 2 > (4 << 30)
+    cu_q = np.array([0, Lq, 2 * Lq, 3 * Lq])
+    cu_k = np.array([0, L, 2 * L, 3 * L])
+    q = inputs.normal(951, (3 * Lq, H_q, D), "bf16")
+    kb = inputs.normal(952, (3, P, H_kv, D), "bf16")
+    vb = inputs.normal(953, (3, P, H_kv, D), "bf16")
+    kd = G.to_device(kb, "bf16").repeat(1, L // P, 1, 1).reshape(3 * L, H_kv, D)
+    vd = G.to_device(vb, "bf16").repeat(1, L // P, 1, 1).reshape(3 * L, H_kv, D)
+    buf, o = _run_varlen(G.to_device(q, "bf16"), kd, vd, cu_q, cu_k, H_q, H_kv, False)
+    got = G.to_f64(o, "bf16")
+    del kd, vd, buf, o
+    torch.cuda.empty_cache()
+    for s in range(3):
+        want = oracle.attention_varlen(_f64(q[s * Lq:(s + 1) * Lq]), _f64(kb[s]), _f64(vb[s]),
+                                       [0, Lq], [0, P], SCALE, False)
+        assert G.max_err(got[s * Lq:(s + 1) * Lq], want) <= G.TOL["bf16"]
