@@ -235,3 +235,37 @@ def test_varlen_packed_kv_beyond_4GiB():
         want = oracle.attention_varlen(_f64(q[s * Lq:(s + 1) * Lq]), _f64(kb[s]), _f64(vb[s]),
                                        [0, Lq], [0, P], SCALE, False)
         assert G.max_err(got[s * Lq:(s + 1) * Lq], want) <= G.TOL["bf16"]
+
+
+def test_qkv_projection_tensors_just_under_2GiB():
+    """X and Q of the fused projection each just under 2 GiB (the host limit:
+    every tensor is addressed with 32-bit offsets), B = 3 sequences of 87,296
+    tokens; X repeats a seeded 256-token block, so output token m equals the
+    oracle's projection of block row m mod 256.  Bound as for the other
+    projection tests: |dY| <= 1e-3 + 2^-8 |Y|."""
+    import oracle.qkv_fp64 as QP
+    torch = G.torch_mod()
+    B, T, dm, H_q, H_kv = 3, 341 * P, 4096, 32, 8
+    M, N = B * T, (H_q + 2 * H_kv) * D
+    assert M * dm * 2 < 2 ** 31 and M * H_q * D * 2 < 2 ** 31 and (M + P) * dm * 2 >= 2 ** 31
+    xb = inputs.normal(971, (P, dm), "bf16")
+    w32 = inputs.bf16_bits_to_f32(inputs.normal(972, (N, dm), "bf16")) / np.float32(np.sqrt(dm))
+    w = inputs.f32_to_bf16_bits(w32)
+    xd = G.to_device(xb, "bf16").repeat(M // P, 1)
+    bq, qo = G.guarded_output((B, H_q, T, D), "bf16")
+    bk, ko = G.guarded_output((B, H_kv, T, D), "bf16")
+    bv, vo = G.guarded_output((B, H_kv, T, D), "bf16")
+    G.note(f"attn_qkv_project B={B} T={T} d_model={dm} H_q={H_q} H_kv={H_kv} D={D} (X, Q near 2 GiB)")
+    abi.attn_qkv_project(xd, G.to_device(w, "bf16"), qo, ko, vo, B, T, dm, H_q, H_kv, D, abi.ATTN_BF16,
+                         torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert all(_guards_intact(b) for b in (bq, bk, bv)), "write outside an output"
+    y = QP.project(_f64(xb), _f64(w))  # [P][N]: the block's projection
+    qn, kn = H_q * D, H_kv * D
+    for b, t in [(0, 0), (0, 255), (1, 5), (1, T - 1), (2, 7), (2, T // 2 + 3), (2, T - 1)]:
+        want = y[(b * T + t) % P]
+        for got, ref in ((qo[b, :, t], want[:qn]), (ko[b, :, t], want[qn:qn + kn]), (vo[b, :, t], want[qn + kn:])):
+            g = G.to_f64(got.reshape(-1), "bf16")
+            assert np.all(np.abs(g - ref) <= 1e-3 + np.abs(ref) * 2.0 ** -8), f"token ({b}, {t})"
+    del xd, bq, qo, bk, ko, bv, vo
+    torch.cuda.empty_cache()
