@@ -98,3 +98,56 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float, num_s
                                page_size, num_pages, max_pages, scale, _dtype_code(q), num_splits,
                                workspace, ws_bytes, s)
     return o
+
+
+def prefill_window(q, k, v, window: int, scale: float, out=None, stream=None):
+    """Causal sliding-window attention: row i (position i + T_kv - T_q) sees
+    its last ``window`` keys.  bf16 [B][H][T][D] tensors."""
+    _check(q, k, v)
+    B, H_q, T_q, D = q.shape
+    _, H_kv, T_kv, _ = k.shape
+    o = torch.empty_like(q) if out is None else out
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    _abi.attn_fwd_prefill_window(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, window, scale,
+                                 _dtype_code(q), s)
+    return o
+
+
+def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                   causal: bool, scale: float, window: int = 0, out=None, stream=None):
+    """Packed batch: q [total_q][H_q][D], k and v [total_k][H_kv][D] (bf16,
+    token-major); int32 cu_seqlens [B + 1] on the GPU give each sequence's
+    rows.  Returns O shaped like q."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q must be [total_q][H_q][D], k and v [total_k][H_kv][D]")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    total_q, H_q, D = q.shape
+    total_k, H_kv, _ = k.shape
+    B = cu_seqlens_q.numel() - 1
+    o = torch.empty_like(q) if out is None else out
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    _abi.attn_fwd_prefill_varlen(q, k, v, o, cu_seqlens_q, cu_seqlens_k, B, H_q, H_kv, D, total_q,
+                                 total_k, max_seqlen_q, max_seqlen_k, causal, window, scale,
+                                 _dtype_code(q), s)
+    return o
+
+
+def qkv_project(x, w, B: int, T: int, H_q: int, H_kv: int, D: int, stream=None):
+    """Fused projection: x [B*T][d_model] and w [(H_q + 2 H_kv) D][d_model]
+    (rows W_Q, then W_K, then W_V) in bf16; returns (q, k, v) head-major,
+    [B][H_q][T][D] and [B][H_kv][T][D]."""
+    for name, t in (("x", x), ("w", w)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D GPU tensor")
+    d_model = x.shape[1]
+    q = torch.empty((B, H_q, T, D), dtype=x.dtype, device=x.device)
+    k = torch.empty((B, H_kv, T, D), dtype=x.dtype, device=x.device)
+    v = torch.empty_like(k)
+    s = torch.cuda.current_stream(x.device) if stream is None else stream
+    _abi.attn_qkv_project(x, w, q, k, v, B, T, d_model, H_q, H_kv, D, _dtype_code(x), s)
+    return q, k, v
