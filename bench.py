@@ -109,14 +109,27 @@ KERNELS = {
     "decode_paged_bf16_B64_T4096_D128_page16": ("decode_split_kernelILi128ELb1E",
                                                 ["decode_bf16.hip", "kernel_common.h"]),
     "qkv_project_bf16_T8192_dmodel4096_N6144": ("qkv_project_kernelILi128E", ["qkv_bf16.hip", "kernel_common.h"]),
+    # the sliding-window line runs the same instantiation as the main prefill (taken from a --only window run)
+    "window_prefill_bf16_T8192_W4096_D128_gqa": ("prefill_bf16_kernelILi128ELb1ELb0ELi1ELi128ELi8E",
+                                                 ["prefill_bf16.hip", "kernel_common.h"]),
+    # prefill<D=128, causal, packed, RB=1, BN=64, 4 waves>
+    "varlen_prefill_bf16_32K_tokens_D128_gqa": ("prefill_bf16_kernelILi128ELb1ELb1ELi1ELi64ELi4E",
+                                                ["prefill_bf16.hip", "kernel_common.h"]),
 }
+# profiles --summarize writes when no names are given
+DEFAULT_SUMMARY = ["prefill_bf16_T8192_D128_gqa", "decode_bf16_B64_T4096_D128",
+                   "decode_paged_bf16_B64_T4096_D128_page16", "qkv_project_bf16_T8192_dmodel4096_N6144"]
 
 
 def algorithmic_bytes(name):
     from transformer_scaled_dot_flash_amd.workloads import DECODE_HEADLINE as wd
     from transformer_scaled_dot_flash_amd.workloads import PREFILL_HEADLINE as wp
-    if name.startswith("prefill"):
-        return wp.bytes()
+    if name.startswith("prefill") or name.startswith("window_prefill"):
+        return wp.bytes()  # the window line reads and writes the same tensors
+    if name.startswith("varlen_prefill"):
+        H_q, H_kv, D = 32, 8, 128
+        n_seq = len(varlen_lengths())
+        return 2 * VARLEN_TOKENS * (2 * H_q + 2 * H_kv) * D + 2 * (n_seq + 1) * 4  # bf16 Q, O, K, V; cu_seqlens
     if name.startswith("decode_paged"):
         return wd.bytes() + wd.B * (wd.T_kv // PAGE_SIZE) * 4 + wd.B * 4  # + block table and lengths
     if name.startswith("decode"):
@@ -133,7 +146,7 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
+def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note, names=None):
     """Turn rocprofv3 CSV output (a --kernel-trace --stats run and two --pmc
     runs, FETCH_SIZE then WRITE_SIZE, each with a device copy of copy_mib MiB
     for calibration) into the summaries kept under profiles/."""
@@ -147,6 +160,14 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
                 out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in out.items()}
 
+    def largest_copy(d, name):
+        # the calibration copy is the largest copy dispatch of the run (small
+        # host-to-device copies, e.g. of cu_seqlens, also run as copy kernels)
+        vals = [float(r["Counter_Value"])
+                for r in _csv_rows(glob.glob(f"{d}/**/*counter_collection.csv", recursive=True)[0])
+                if r["Counter_Name"] == name and "copyBuffer" in r["Kernel_Name"]]
+        return max(vals) if vals else None
+
     fetch = counter(fetch_dir, "FETCH_SIZE")
     write = counter(write_dir, "WRITE_SIZE")
     copy_bytes = copy_mib << 20
@@ -155,13 +176,14 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note):
         ks = [k for k in d if sub in k]
         return d[ks[0]] if ks else None
 
-    f_copy = pick(fetch, "copyBuffer")
-    w_copy = pick(write, "copyBuffer")
+    f_copy = largest_copy(fetch_dir, "FETCH_SIZE")
+    w_copy = largest_copy(write_dir, "WRITE_SIZE")
     f_scale = copy_bytes / (f_copy * 1024.0)
     w_scale = copy_bytes / (w_copy * 1024.0)
     csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
-    algo = {name: algorithmic_bytes(name) for name in KERNELS}
-    for name, (sub, files) in KERNELS.items():
+    algo = {name: algorithmic_bytes(name) for name in (names or DEFAULT_SUMMARY)}
+    for name in (names or DEFAULT_SUMMARY):
+        sub, files = KERNELS[name]
         st = [r for r in stats if sub in r["Name"]]
         if not st or pick(fetch, sub) is None or pick(write, sub) is None:
             continue
@@ -306,21 +328,30 @@ def window_prefill_line(abi, torch, wp, qp, kp, vp, stream, warmup, settle, step
                                     wp.scale, abi.ATTN_BF16, stream)
     log("window prefill")
     avg, mn = time_calls(torch, stream, run, warmup, settle, steps)
-    return mfma_line("sliding-window prefill TFLOP/s",
+    line = mfma_line("sliding-window prefill TFLOP/s",
                      f"causal GQA B=1 H_q=32 H_kv=8 T=8192 D=128 bf16, window {W}", flops, avg, mn,
                      "prefill_bf16_kernel<D=128,causal,BN=128,8 waves> (window)")
+    line["roofline"]["traffic"] = profile_traffic("window_prefill_bf16_T8192_W4096_D128_gqa")
+    return line
+
+
+def varlen_lengths():
+    """Sequence lengths of the packed-batch line: drawn once from a seeded
+    uniform on [128, 4096] until VARLEN_TOKENS tokens, the last one cut."""
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    lens = []
+    while sum(lens) < VARLEN_TOKENS:
+        lens.append(int(rng.integers(128, 4097)))
+    lens[-1] -= sum(lens) - VARLEN_TOKENS
+    return [x for x in lens if x > 0]
 
 
 def varlen_prefill_line(abi, torch, np, stream, dev, warmup, settle, steps):
     """Packed causal GQA batch of mixed lengths (H_q=32, H_kv=8, D=128, bf16):
     lengths drawn once from a seeded uniform on [128, 4096], 32K tokens."""
     from transformer_scaled_dot_flash_amd import inputs
-    rng = np.random.default_rng(2024)
-    lens = []
-    while sum(lens) < VARLEN_TOKENS:
-        lens.append(int(rng.integers(128, 4097)))
-    lens[-1] -= sum(lens) - VARLEN_TOKENS
-    lens = [x for x in lens if x > 0]
+    lens = varlen_lengths()
     H_q, H_kv, D = 32, 8, 128
     total = sum(lens)
     cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
@@ -343,6 +374,7 @@ def varlen_prefill_line(abi, torch, np, stream, dev, warmup, settle, steps):
                      f"{total} tokens, H_q=32 H_kv=8 D=128 bf16", flops, avg, mn,
                      "prefill_bf16_kernel<D=128,causal,packed,BN=64,4 waves>")
     line["config"]["lengths"] = lens
+    line["roofline"]["traffic"] = profile_traffic("varlen_prefill_bf16_32K_tokens_D128_gqa")
     return line
 
 
@@ -445,8 +477,8 @@ def main():
         summarize_counters(sys.argv[3:], sys.argv[2])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
-        # python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR COPY_MIB "commands"
-        summarize(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6])
+        # python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR COPY_MIB "commands" [NAME ...]
+        summarize(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7:] or None)
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
