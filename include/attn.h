@@ -33,7 +33,8 @@
  *
  * Ownership and asynchrony: the caller owns every buffer, including the
  * decode workspace; the library keeps no pointer after a call returns and
- * allocates no device memory.  Calls only enqueue work on `stream` (a
+ * allocates no device memory (the one static device array it holds, the
+ * scratch of attn_fwd_decode_noalloc, comes with the loaded code object).  Calls only enqueue work on `stream` (a
  * hipStream_t; NULL is the null stream) and never synchronise.  Launch
  * failures return ATTN_ERR_HIP (attn_last_hip_error() gives the HIP code
  * of the calling thread's last failure); faults inside a kernel surface at
@@ -45,7 +46,10 @@
  * the call returns ATTN_OK, launches nothing and ignores the pointers.
  *
  * Thread safety: all functions are re-entrant; the library holds no mutable
- * state except the per-thread last HIP error.  Results are bitwise
+ * host state except the per-thread last HIP error and the per-device
+ * address of that scratch array (looked up once, under a lock); calls to
+ * attn_fwd_decode_noalloc that overlap on one GPU share the array's
+ * contents (see there).  Results are bitwise
  * deterministic for fixed arguments (including the decode split count).
  */
 #ifndef ATTN_H
@@ -57,7 +61,10 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
+
+/* Bytes of the static device scratch behind attn_fwd_decode_noalloc. */
+#define ATTN_DECODE_SCRATCH_BYTES (16u << 20)
 
 typedef enum attn_status {
     ATTN_OK = 0,
@@ -71,7 +78,9 @@ typedef enum attn_status {
     ATTN_ERR_ALIGNMENT = 5,      /* a pointer is not 16-byte aligned          */
     ATTN_ERR_ALIAS = 6,          /* O overlaps Q, K or V (or the workspace)   */
     ATTN_ERR_WORKSPACE = 7,      /* decode workspace too small                */
-    ATTN_ERR_HIP = 8             /* a HIP launch call failed                  */
+    ATTN_ERR_HIP = 8,            /* a HIP launch call failed                  */
+    ATTN_ERR_SCRATCH = 9         /* attn_fwd_decode_noalloc: the split plan   */
+                                 /* needs more than ATTN_DECODE_SCRATCH_BYTES */
 } attn_status_t;
 
 typedef enum attn_dtype {
@@ -173,6 +182,26 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
                               int B, int H_q, int H_kv, int T_q, int T_kv, int D,
                               int causal, float scale, int dtype, int num_splits,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode without a workspace argument and without any device allocation,
+ * for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments (minus
+ * the workspace), checks, split plan, kernels and results, bit for bit, as
+ * attn_fwd_decode.  The split partials go to a static device array of
+ * ATTN_DECODE_SCRATCH_BYTES (16 MiB) that the library holds on every GPU it
+ * runs on until the process ends; the first call on a device looks up that
+ * device's copy (hipGetSymbolAddress, with the stream's device current).  A
+ * split plan needing more (B * H_q * splits * (D + 2) * 4 bytes; the default
+ * plan needs at most about 8.5 MiB) returns ATTN_ERR_SCRATCH before anything
+ * is launched.  All calls on one GPU share its array, and nothing in it has
+ * to start at zero: calls that may run at the same time on one GPU (other
+ * streams, other threads) race on it and must be ordered by the caller.
+ */
+attn_status_t attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                      int B, int H_q, int H_kv, int T_q, int T_kv, int D,
+                                      int causal, float scale, int dtype, int num_splits,
+                                      void* stream);
 
 /*
  * Decode over a paged KV cache (the serving form of decode; Ch. 11 page,

@@ -12,7 +12,7 @@ import transformer_scaled_dot_flash_amd.attn as A
 ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "attn.h"
 
-OK, NULL, SHAPE, UNSUP, SCALE, ALIGN, ALIAS, WS, HIP = range(9)
+OK, NULL, SHAPE, UNSUP, SCALE, ALIGN, ALIAS, WS, HIP, SCRATCH = range(10)
 BF16, F32 = A.ATTN_BF16, A.ATTN_F32
 
 # Fake, well-separated, 16-byte aligned device addresses: never dereferenced,
@@ -36,8 +36,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert A.attn_abi_version() == 1
-    for st in range(9):
+    assert A.attn_abi_version() == 2
+    for st in range(10):
         assert A.attn_status_string(st) and A.attn_status_string(st) != "unknown status"
     assert A.attn_status_string(99) == "unknown status"
 
@@ -130,6 +130,53 @@ def test_decode_workspace_size():
 def test_decode_workspace_too_small_by_one_byte():
     need = A.attn_fwd_decode_workspace_bytes(2, 8, 2, 300, 128, BF16, 0)
     assert decode(ws_bytes=need - 1) == WS
+
+
+def decode_noalloc(q=QP, k=KP, v=VP, o=OP, B=2, H_q=8, H_kv=2, T_q=1, T_kv=300, D=128, scale=0.1,
+                   dtype=BF16, splits=0):
+    return A.attn_fwd_decode_noalloc(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, 0, scale, dtype, splits,
+                                     None, check=False)
+
+
+SCRATCH_BYTES = 16 << 20
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(T_q=2), UNSUP), (dict(splits=-1), UNSUP), (dict(splits=1025), UNSUP), (dict(D=32), UNSUP),
+    (dict(H_q=8, H_kv=3), SHAPE), (dict(T_kv=0), SHAPE), (dict(scale=float("nan")), SCALE),
+    (dict(q=0), NULL), (dict(o=0), NULL), (dict(v=VP + 8), ALIGN), (dict(o=KP + 32), ALIAS),
+    # 64 * 32 * 64 splits * 130 fp32 = 68 MB of partials: more than the static scratch
+    (dict(B=64, H_q=32, H_kv=8, T_kv=4096, splits=64, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40),
+     SCRATCH),
+])
+def test_decode_noalloc_rejects(kw, want):
+    assert decode_noalloc(**kw) == want
+
+
+def test_decode_noalloc_scratch_limit_is_exact():
+    # the largest plan that fits is accepted by validation (checked on an
+    # empty batch: nothing launched); one split more needs too much
+    B, H_q, H_kv, T_kv, D = 4, 32, 8, 1 << 20, 128
+    per_split = B * H_q * (D + 2) * 4
+    fits = SCRATCH_BYTES // per_split
+    assert A.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, BF16, fits) <= SCRATCH_BYTES
+    assert A.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, BF16, fits + 1) > SCRATCH_BYTES
+    far = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40)  # 1 GiB K and V: well apart
+    assert decode_noalloc(B=B, H_q=H_q, H_kv=H_kv, T_kv=T_kv, splits=fits + 1, **far) == SCRATCH
+    assert decode_noalloc(B=0, H_q=H_q, H_kv=H_kv, T_kv=T_kv, splits=fits, q=0, k=0, v=0, o=0) == OK
+
+
+def test_decode_noalloc_default_plans_fit_the_scratch():
+    # the default split plan of every shape with up to 64 q heads per kv head
+    # needs at most ~8.5 MiB of partials, within the static scratch
+    worst = 0
+    for B in (1, 2, 3, 4, 8, 16, 64):
+        for H_kv in (1, 2, 8):
+            for G in (1, 4, 8, 32, 64):
+                for T in (64, 4096, 32768, 1 << 20):
+                    worst = max(worst, A.attn_fwd_decode_workspace_bytes(B, G * H_kv, H_kv, T, 128,
+                                                                         BF16, 0))
+    assert 0 < worst <= SCRATCH_BYTES
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -29,6 +29,7 @@ STATUS_NAMES = {
     6: "ATTN_ERR_ALIAS",
     7: "ATTN_ERR_WORKSPACE",
     8: "ATTN_ERR_HIP",
+    9: "ATTN_ERR_SCRATCH",
 }
 
 EXPORTED = (
@@ -36,6 +37,7 @@ EXPORTED = (
     "attn_fwd_prefill_window",
     "attn_fwd_prefill_varlen",
     "attn_fwd_decode",
+    "attn_fwd_decode_noalloc",
     "attn_fwd_decode_workspace_bytes",
     "attn_fwd_decode_default_splits",
     "attn_fwd_decode_paged",
@@ -91,6 +93,8 @@ def load_library(path: Path | str | None = None):
     lib.attn_fwd_prefill_varlen.restype = i
     lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.attn_fwd_decode.restype = i
+    lib.attn_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd_decode_noalloc.restype = i
     lib.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.attn_fwd_decode_workspace_bytes.restype = sz
     lib.attn_fwd_decode_default_splits.argtypes = [i, i, i, i, i]
@@ -175,6 +179,17 @@ def attn_fwd_decode(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, causal, scale, dtype
                              workspace_bytes, _stream(stream))
     if check:
         _check(st, "attn_fwd_decode")
+    return st
+
+
+def attn_fwd_decode_noalloc(q, k, v, o, B, H_q, H_kv, T_q, T_kv, D, causal, scale, dtype,
+                            num_splits, stream=None, check=True) -> int:
+    lib = load_library()
+    st = lib.attn_fwd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H_q, H_kv, T_q, T_kv, D,
+                                     1 if causal else 0, float(scale), dtype, num_splits,
+                                     _stream(stream))
+    if check:
+        _check(st, "attn_fwd_decode_noalloc")
     return st
 
 

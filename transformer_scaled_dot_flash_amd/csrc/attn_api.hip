@@ -4,6 +4,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "attn.h"
 #include "kernel_common.h"
 
@@ -131,6 +133,104 @@ attn_status_t check_paged_params(int B, int H_q, int H_kv, int D, int page_size,
     if ((long long)max_pages * page_size > (1LL << 30)) return ATTN_ERR_INVALID_SHAPE;
     const long long waves = (long long)B * H_kv * ((H_q / H_kv + 31) / 32) * kMaxSplits;
     if (waves / 4 > 0x7fffffffLL || (long long)B * H_q > 0x7fffffffLL) return ATTN_ERR_INVALID_SHAPE;
+    return ATTN_OK;
+}
+
+// The bf16 decode launch shared by attn_fwd_decode and
+// attn_fwd_decode_noalloc: `ws` holds the split partials (unused with one
+// split).
+attn_status_t decode_bf16(const void* q, const void* k, const void* v, void* o, int B, int H_q,
+                          int H_kv, int T_kv, int D, float scale, const SplitPlan& p, void* ws,
+                          hipStream_t s) {
+    attn::DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.T_kv = T_kv;
+    a.D = D;
+    positive_scale(scale, &a.c_log2, &a.neg_q);
+    a.n_splits = p.n_splits;
+    a.keys_per_split = p.keys_per_split;
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_ml = ws ? a.ws_o + (size_t)B * H_q * p.n_splits * D : nullptr;
+    return hip_status(attn::launch_decode_bf16(a, s));
+}
+
+// fp32 decode: the fp32 forward with one query row (no workspace).
+attn_status_t decode_f32(const void* q, const void* k, const void* v, void* o, int B, int H_q,
+                         int H_kv, int T_kv, int D, float scale, hipStream_t s) {
+    attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.T_q = 1;
+    a.T_kv = T_kv;
+    a.D = D;
+    a.causal = 0;
+    a.scale = scale;
+    a.scale_log2 = log2_scale(scale);
+    positive_scale(scale, &a.c_log2, &a.neg_q);
+    return hip_status(attn::launch_prefill_f32(a, s));
+}
+
+// Checks every decode entry point shares (before any pointer is looked at).
+attn_status_t check_decode_params(int B, int H_q, int H_kv, int T_q, int T_kv, int D, int dtype,
+                                  float scale, int num_splits) {
+    attn_status_t st = check_params(B, H_q, H_kv, T_q, T_kv, D, dtype, scale);
+    if (st != ATTN_OK) return st;
+    if (T_q != 1) return ATTN_ERR_UNSUPPORTED;
+    if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_UNSUPPORTED;
+    const long long waves = (long long)B * H_kv * ((H_q / H_kv + 31) / 32) * kMaxSplits;
+    if (waves / 4 > 0x7fffffffLL || (long long)B * H_q > 0x7fffffffLL) return ATTN_ERR_INVALID_SHAPE;
+    return ATTN_OK;
+}
+
+// Scratch of the no-allocation decode: the split partials of one call live
+// here instead of in a caller's workspace.  Each GPU the library runs on
+// holds its own copy from the module's load until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: only the
+// address returned by hipGetSymbolAddress (one per device) is passed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each device (nullptr: not looked up)
+
+// Device address of `scratch` on the device `s` launches on, looked up once
+// per device with that device current.
+attn_status_t scratch_for_stream(hipStream_t s, void** out) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    int dev = cur;
+    if (s != nullptr) {
+        hipDevice_t d = -1;
+        e = hipStreamGetDevice(s, &d);
+        if (e != hipSuccess) return hip_status(e);
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e_back = (dev != cur) ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return hip_status(e);
+        if (e_back != hipSuccess) return hip_status(e_back);
+        if (p == nullptr) return hip_status(hipErrorInvalidSymbol);
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
     return ATTN_OK;
 }
 
@@ -263,36 +363,14 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
                               int H_q, int H_kv, int T_q, int T_kv, int D, int causal,
                               float scale, int dtype, int num_splits, void* workspace,
                               size_t workspace_bytes, void* stream) {
-    attn_status_t st = check_params(B, H_q, H_kv, T_q, T_kv, D, dtype, scale);
+    attn_status_t st = check_decode_params(B, H_q, H_kv, T_q, T_kv, D, dtype, scale, num_splits);
     if (st != ATTN_OK) return st;
-    if (T_q != 1) return ATTN_ERR_UNSUPPORTED;
-    if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_UNSUPPORTED;
-    const long long waves = (long long)B * H_kv * ((H_q / H_kv + 31) / 32) * kMaxSplits;
-    if (waves / 4 > 0x7fffffffLL || (long long)B * H_q > 0x7fffffffLL) return ATTN_ERR_INVALID_SHAPE;
     (void)causal;  // one query row at the end of the keys sees every key
     if (B == 0) return ATTN_OK;
     st = check_tensors(q, k, v, o, B, H_q, H_kv, 1, T_kv, D, dtype);
     if (st != ATTN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-
-    if (dtype == ATTN_F32) {
-        attn::PrefillArgs a{};
-        a.q = q;
-        a.k = k;
-        a.v = v;
-        a.o = o;
-        a.B = B;
-        a.H_q = H_q;
-        a.H_kv = H_kv;
-        a.T_q = 1;
-        a.T_kv = T_kv;
-        a.D = D;
-        a.causal = 0;
-        a.scale = scale;
-        a.scale_log2 = log2_scale(scale);
-        positive_scale(scale, &a.c_log2, &a.neg_q);
-        return hip_status(attn::launch_prefill_f32(a, s));
-    }
+    if (dtype == ATTN_F32) return decode_f32(q, k, v, o, B, H_q, H_kv, T_kv, D, scale, s);
 
     const SplitPlan p = plan_splits(B, H_q, H_kv, T_kv, num_splits);
     const size_t need = decode_ws_bytes(B, H_q, D, p);
@@ -304,23 +382,32 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
     if (overlaps(workspace, need, o, nq) || overlaps(workspace, need, q, nq) ||
         overlaps(workspace, need, k, nkv) || overlaps(workspace, need, v, nkv))
         return ATTN_ERR_ALIAS;
+    return decode_bf16(q, k, v, o, B, H_q, H_kv, T_kv, D, scale, p, workspace, s);
+}
 
-    attn::DecodeArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.B = B;
-    a.H_q = H_q;
-    a.H_kv = H_kv;
-    a.T_kv = T_kv;
-    a.D = D;
-    positive_scale(scale, &a.c_log2, &a.neg_q);
-    a.n_splits = p.n_splits;
-    a.keys_per_split = p.keys_per_split;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = a.ws_o + (size_t)B * H_q * p.n_splits * D;
-    return hip_status(attn::launch_decode_bf16(a, s));
+attn_status_t attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, int B,
+                                      int H_q, int H_kv, int T_q, int T_kv, int D, int causal,
+                                      float scale, int dtype, int num_splits, void* stream) {
+    attn_status_t st = check_decode_params(B, H_q, H_kv, T_q, T_kv, D, dtype, scale, num_splits);
+    if (st != ATTN_OK) return st;
+    (void)causal;
+    if (B == 0) return ATTN_OK;
+    st = check_tensors(q, k, v, o, B, H_q, H_kv, 1, T_kv, D, dtype);
+    if (st != ATTN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == ATTN_F32) return decode_f32(q, k, v, o, B, H_q, H_kv, T_kv, D, scale, s);
+
+    const SplitPlan p = plan_splits(B, H_q, H_kv, T_kv, num_splits);
+    const size_t need = decode_ws_bytes(B, H_q, D, p);
+    if (need > (size_t)ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        // The split pass overwrites every partial it hands to the combine
+        // pass, so nothing in the scratch has to start at zero.
+        st = scratch_for_stream(s, &ws);
+        if (st != ATTN_OK) return st;
+    }
+    return decode_bf16(q, k, v, o, B, H_q, H_kv, T_kv, D, scale, p, ws, s);
 }
 
 size_t attn_fwd_decode_workspace_bytes(int B, int H_q, int H_kv, int T_kv, int D, int dtype,
@@ -447,6 +534,7 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_ALIAS: return "output overlaps an input or the workspace";
         case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
         case ATTN_ERR_HIP: return "HIP launch failed";
+        case ATTN_ERR_SCRATCH: return "decode needs more scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }
