@@ -111,3 +111,62 @@ def bf16_floor(want: np.ndarray) -> float:
     """max |bf16_RNE(O_ref) - O_ref|: the error of a perfectly rounded output."""
     r = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(want.astype(np.float32))).astype(np.float64)
     return float(np.max(np.abs(r - want))) if want.size else 0.0
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |x|: 2^(e - 8) for |x| in [2^e, 2^(e + 1)) (bf16
+    keeps 8 significant bits), 2^-134 below the normal range."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 8)
+
+
+def arithmetic_bound(p_rows: np.ndarray, v: np.ndarray, o_rows: np.ndarray) -> np.ndarray:
+    """Per-element error bound of a bf16-output kernel that rounds the
+    softmax weights to bf16 before P V, accumulates in fp32 and rounds O once
+    (the arithmetic stated in include/attn.h), for the rows whose exact
+    weights are p_rows [n, T_kv] and exact outputs o_rows [n, D]:
+
+      weights: each p_j is stored as p_j (1 + eta_j) with |eta_j| <= 2^-9
+        (round to nearest bf16), and O is normalised by the sum of the
+        stored weights, so O moves by sum_j w_j eta_j (v_j - O) / (1 + eta_bar),
+        at most 2^-9 sum_j w_j |v_j - O| (1 + 2^-8); 2^-10 more covers the
+        fp32 score and exponent errors (relative ~1e-4 of a weight at the
+        workloads' logits);
+      fp32 sums over T_kv keys (O and the weight sum): 2 T_kv 2^-24
+        sum_j w_j |v_j| each;
+      the final rounding: half a bf16 ulp of the (perturbed) value.
+    """
+    T = p_rows.shape[1]
+    dev = np.einsum("ij,ijd->id", p_rows, np.abs(v[None, :, :] - o_rows[:, None, :]))
+    mag = p_rows @ np.abs(v)
+    a = (2.0 ** -9 * (1 + 2.0 ** -8) + 2.0 ** -10) * dev + 4 * T * 2.0 ** -24 * mag
+    return bf16_half_ulp(np.abs(o_rows) + a) + a
+
+
+def check_bf16_prefill(got, want, Q, K, V, scale, causal, window=0, what=""):
+    """Compare a bf16 output with the oracle element by element.  The bar is
+    max|dO| <= 1.5e-2; an element over it passes only if the bar is below
+    what the bf16 output format allows there (half an ulp of O_ref is 1/64
+    once |O_ref| >= 4, beyond 1.5e-2), and then only within
+    arithmetic_bound, recomputed from the oracle's own weights for that row.
+    Returns (max|dO|, bf16 floor of O_ref, elements judged by the bound)."""
+    import oracle
+    err = np.abs(got - want)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    floor = bf16_floor(want)
+    over = np.argwhere(err > TOL["bf16"])
+    n_bound = 0
+    B, H_q, T_q, D = want.shape
+    H_kv = K.shape[1]
+    for b, h, i in {(int(b), int(h), int(i)) for b, h, i, _ in over}:
+        g = oracle.kv_head_for(h, H_q, H_kv)
+        o_ref, p = oracle.attention_head(Q[b, h], K[b, g], V[b, g], scale, causal, rows=[i],
+                                         return_p=True, window=window)
+        bound = arithmetic_bound(p, V[b, g], o_ref)[0]
+        e_row = err[b, h, i]
+        bad = (e_row > TOL["bf16"]) & (e_row > bound)
+        assert not bad.any(), (f"{what}: row (b={b}, h={h}, i={i}) max|dO| {e_row.max():.4e} over the bar "
+                               f"and over its arithmetic bound {bound[np.argmax(e_row)]:.4e} "
+                               f"(|O_ref| {abs(o_ref[0, np.argmax(e_row)]):.3f})")
+        n_bound += int((e_row > TOL["bf16"]).sum())
+    return float(err.max()) if err.size else 0.0, floor, n_bound

@@ -2,9 +2,12 @@
 element by element on the same seeded inputs.
 
 Bar: max |O_gpu - O_oracle| <= 1e-5 for fp32 tensors and <= 1.5e-2 for bf16
-tensors, over every compared element.  Also checked on every call: no write
-outside O (sentinel guard bands) and no element of O left unwritten (O starts
-as NaN)."""
+tensors, over every compared element.  Where the bf16 output format itself
+cannot meet 1.5e-2 (|O| >= 4, half an ulp is 1/64; only at scales well above
+1/sqrt(D)), an element is judged by its own arithmetic bound instead
+(gpu_util.check_bf16_prefill); the workloads must meet the plain bar.  Also
+checked on every call: no write outside O (sentinel guard bands) and no
+element of O left unwritten (O starts as NaN)."""
 import math
 import zlib
 
@@ -37,33 +40,54 @@ def f64(x, dtype):
 
 
 # --- the five workloads ----------------------------------------------------------
-C4_ROWS = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, 1023, 4095, 4096, 8064, 8127, 8128,
-           8190, 8191]
-
-
 @pytest.mark.parametrize("ordinal", [1, 2, 3, 4, 5])
 def test_workload_parity(ordinal):
+    """Every element of every workload's output against the oracle (the
+    T=8192 GQA prefill too: 32 heads x 8192 rows, ~15 s of host time)."""
     w = BY_ORDINAL[ordinal]
     q, k, v = w.make_inputs()
     Q, K, V = f64(q, w.dtype), f64(k, w.dtype), f64(v, w.dtype)
     if w.kind == "decode":
         got = G.decode(q, k, v, w.scale, w.dtype)
-        want = oracle.attention(Q, K, V, w.scale, w.causal)
-    elif ordinal == 4:
-        got_full = G.prefill(q, k, v, w.causal, w.scale, w.dtype)
-        rng = np.random.default_rng(4)
-        rows = sorted(set(C4_ROWS) | set(rng.integers(0, w.T_q, 44).tolist()))
-        got = got_full[:, :, rows]
-        want = oracle.attention(Q, K, V, w.scale, w.causal, rows=rows)
-        # properties that hold on every row of the full output
-        assert np.all(np.isfinite(got_full))
-        assert np.array_equal(got_full[:, :, 0], V[:, np.arange(w.H_q) // (w.H_q // w.H_kv), 0])
     else:
         got = G.prefill(q, k, v, w.causal, w.scale, w.dtype)
-        want = oracle.attention(Q, K, V, w.scale, w.causal)
-    err = G.max_err(got, want)
-    print(f"{w.name}: max|dO| = {err:.3e} (bf16 floor {G.bf16_floor(want):.3e})")
-    assert err <= G.TOL[w.dtype], f"{w.name}: max|dO| {err:.3e} > {G.TOL[w.dtype]}"
+    want = oracle.attention(Q, K, V, w.scale, w.causal)
+    if ordinal == 4:
+        # causal row 0 sees only key 0: O equals V[0] bit for bit
+        assert np.array_equal(got[:, :, 0], V[:, np.arange(w.H_q) // (w.H_q // w.H_kv), 0])
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    if w.dtype == "bf16":
+        err, floor, n_bound = G.check_bf16_prefill(got, want, Q, K, V, w.scale, w.causal, what=w.name)
+        print(f"{w.name}: max|dO| = {err:.3e}, bf16 floor {floor:.3e}, rel. Frobenius {rel:.3e}, "
+              f"elements judged by the arithmetic bound: {n_bound}")
+        assert n_bound == 0 and err <= G.TOL["bf16"], f"{w.name}: max|dO| {err:.3e}"
+    else:
+        err = G.max_err(got, want)
+        print(f"{w.name}: max|dO| = {err:.3e}, rel. Frobenius {rel:.3e}")
+        assert err <= G.TOL[w.dtype], f"{w.name}: max|dO| {err:.3e} > {G.TOL[w.dtype]}"
+
+
+# Shapes and seeds (found by a CPU scan) whose exact output has rows with
+# |O| >= 4 at scale 4/sqrt(D): there half a bf16 ulp is 1/64, so even the
+# correctly rounded exact result misses 1.5e-2 and the per-element
+# arithmetic bound judges those elements.
+FLOOR_CASES = [(185, 1, 8, 2, 128, 128, False), (334, 1, 8, 1, 128, 64, True)]
+
+
+@pytest.mark.parametrize("case", FLOOR_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bf16_output_floor_cases(case):
+    seed, B, H_q, H_kv, T, D, causal = case
+    q = gen(seed, (B, H_q, T, D), "bf16")
+    k = gen(seed + 1, (B, H_kv, T, D), "bf16")
+    v = gen(seed + 2, (B, H_kv, T, D), "bf16")
+    Q, K, V = f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16")
+    scale = float(np.float32(4.0 / math.sqrt(D)))
+    want = oracle.attention(Q, K, V, scale, causal)
+    assert G.bf16_floor(want) > G.TOL["bf16"]
+    got = G.prefill(q, k, v, causal, scale, "bf16")
+    err, floor, n_bound = G.check_bf16_prefill(got, want, Q, K, V, scale, causal, what=str(case))
+    print(f"{case}: max|dO| = {err:.4e}, bf16 floor {floor:.4e}, judged by the bound: {n_bound}")
+    assert err <= 2 * floor
 
 
 # --- ragged and edge shapes ----------------------------------------------------------
