@@ -13,6 +13,15 @@ causal FLOPs counted once (4*D per visible (query, key) pair per q head);
 the decode KV-read rate in GB/s is reported beside it.  Kernel durations come
 from HIP events recorded on the stream the kernels run on.
 
+Beside the step: lines for the paged decode, sliding window, packed batch,
+QKV projection, the three small workloads (B1 H1 T128 fp32, B1 H4 T128,
+B4 H12 T1024) and a long-context decode whose keys are split (B=4,
+T_kv=32768); measured ceilings (register-fed MFMA loop, 1 GiB streaming
+read, shader clock during the prefill) beside the published peaks; the
+timed outputs of the prefill (the heads the CPU baseline computed) and of
+the decode compared with the oracle (max|dO|, relative Frobenius error, bf16
+floor).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -32,6 +41,7 @@ sys.path.insert(0, str(ROOT))
 METRIC = "attention fwd TFLOP/s (causal GQA T=8K prefill); decode KV-read GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs, 2.4 GHz)
 PROFILES = ROOT / "profiles"
 
 
@@ -65,39 +75,77 @@ def traffic_from_profile(name, digest):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_info():
+    """Host facts for the CPU baseline: logical CPUs, CPUs this process may
+    run on, the BLAS thread pool numpy uses, and the CPU model."""
+    info = {"host_logical_cpus": os.cpu_count(), "affinity_cpus": None, "blas_threads": None,
+            "cpu_model": None}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas_threads"] = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        pass
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(budget_s=15.0):
     """The CPU oracle, timed on this host on a bounded sample of the prefill
     workload: q heads in order, every query row of each, until the budget is
-    spent (at least one head)."""
+    spent (at least one head).  Returns (record, {head: oracle output})."""
     import numpy as np
     import oracle
     from transformer_scaled_dot_flash_amd import inputs
     from transformer_scaled_dot_flash_amd.workloads import PREFILL_HEADLINE as w
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     q, k, v = w.make_inputs()
     Q, K, V = (inputs.as_f64(x, w.dtype) for x in (q, k, v))
     rows = np.arange(0, w.T_q)
     flop_per_head = sum(4 * w.D * (int(i) + 1) for i in rows)
     done = 0
+    outs = {}
     t0 = time.perf_counter()
     for h in range(w.H_q):
-        oracle.attention(Q, K, V, w.scale, w.causal, rows=rows, heads=[h])
+        outs[h] = oracle.attention(Q, K, V, w.scale, w.causal, rows=rows, heads=[h])[0, 0]
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {
+    ci = cpu_info()
+    rec = {
         "value": round(done * flop_per_head / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": ci["affinity_cpus"] or ci["host_logical_cpus"],
         "kind": "oracle",
         "sample": f"{done} of {w.H_q} q heads x all {rows.size} query rows of the "
-                  f"T=8192 causal GQA prefill, float64 three-stage oracle, {dt:.1f} s",
+                  f"T=8192 causal GQA prefill, float64 three-stage oracle, {dt:.1f} s "
+                  f"(the oracle forms each head's full 8192 x 8192 score block before masking, "
+                  f"so it executes about twice the causal FLOPs it is credited with)",
+        **ci,
     }
+    return rec, outs
+
+
+def parity_stats(got, want):
+    """max|dO|, relative Frobenius error and the bf16 floor
+    max|bf16_RNE(O_ref) - O_ref| (the error of a correctly rounded output)."""
+    import numpy as np
+    from transformer_scaled_dot_flash_amd import inputs
+    err = float(np.max(np.abs(got - want)))
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    r = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(want.astype(np.float32))).astype(np.float64)
+    floor = float(np.max(np.abs(r - want)))
+    return {"max_abs_err": float(f"{err:.4g}"), "rel_frobenius": float(f"{rel:.4g}"),
+            "bf16_floor": float(f"{floor:.4g}"), "tolerance": 1.5e-2, "pass": err <= 1.5e-2}
 
 
 KERNELS = {
@@ -115,6 +163,12 @@ KERNELS = {
     # prefill<D=128, causal, packed, RB=1, BN=64, 4 waves>
     "varlen_prefill_bf16_32K_tokens_D128_gqa": ("prefill_bf16_kernelILi128ELb1ELb1ELi1ELi64ELi4E",
                                                 ["prefill_bf16.hip", "kernel_common.h"]),
+    # prefill<D=64, causal, contiguous, RB=1, BN=64, 4 waves>: the GPT-2-small workload
+    "prefill_bf16_gpt2s_B4_H12_T1024_D64": ("prefill_bf16_kernelILi64ELb1ELb0ELi1ELi64ELi4E",
+                                            ["prefill_bf16.hip", "kernel_common.h"]),
+    # long-context decode with split keys: split pass and combine pass
+    "decode_split_bf16_B4_T32768_D128": ("decode_split_kernelILi128ELb0E", ["decode_bf16.hip", "kernel_common.h"]),
+    "decode_combine_bf16_B4_T32768_D128": ("decode_combine_kernel<128>", ["decode_bf16.hip", "kernel_common.h"]),
 }
 # profiles --summarize writes when no names are given
 DEFAULT_SUMMARY = ["prefill_bf16_T8192_D128_gqa", "decode_bf16_B64_T4096_D128",
@@ -124,6 +178,15 @@ DEFAULT_SUMMARY = ["prefill_bf16_T8192_D128_gqa", "decode_bf16_B64_T4096_D128",
 def algorithmic_bytes(name):
     from transformer_scaled_dot_flash_amd.workloads import DECODE_HEADLINE as wd
     from transformer_scaled_dot_flash_amd.workloads import PREFILL_HEADLINE as wp
+    if name.startswith("prefill_bf16_gpt2s"):
+        from transformer_scaled_dot_flash_amd.workloads import BY_ORDINAL
+        return BY_ORDINAL[3].bytes()
+    if name.startswith("decode_split"):
+        B, H_q, H_kv, T, D, S = LONG_DECODE
+        return 2 * (2 * B * H_kv * T * D + B * H_q * D) + B * H_q * S * (D + 2) * 4  # K, V, Q; partials written
+    if name.startswith("decode_combine"):
+        B, H_q, H_kv, T, D, S = LONG_DECODE
+        return B * H_q * S * (D + 2) * 4 + 2 * B * H_q * D  # partials read, O written
     if name.startswith("prefill") or name.startswith("window_prefill"):
         return wp.bytes()  # the window line reads and writes the same tensors
     if name.startswith("varlen_prefill"):
@@ -146,10 +209,57 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note, names=None):
+def timed_dispatches(trace_dir, sub, n_timed):
+    """Durations (us) of the last n_timed dispatches of the kernel whose name
+    contains sub in a --kernel-trace run: the bench's timed calls come after
+    its warm-up, so these are the dispatches its events measured."""
+    import glob
+    rows = _csv_rows(glob.glob(f"{trace_dir}/**/*kernel_trace.csv", recursive=True)[0])
+    d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows if sub in r["Kernel_Name"])
+    return [(e - b) / 1e3 for b, e in d[-n_timed:]]
+
+
+def bench_line_from_log(log_path):
+    """The JSON line a profiled bench run printed (or None)."""
+    try:
+        for line in Path(log_path).read_text().splitlines():
+            if line.startswith("{"):
+                return json.loads(line)
+    except OSError:
+        pass
+    return None
+
+
+def bench_event_us(line, name):
+    """The bench's HIP-event average for the line a profile covers."""
+    if not line:
+        return None
+    path = {
+        "prefill_bf16_T8192_D128_gqa": ("roofline", "avg_launch_us"),
+        "decode_bf16_B64_T4096_D128": ("decode", "roofline", "avg_call_us"),
+        "decode_paged_bf16_B64_T4096_D128_page16": ("paged_decode", "roofline", "avg_call_us"),
+        "qkv_project_bf16_T8192_dmodel4096_N6144": ("qkv_projection", "roofline", "avg_launch_us"),
+        "window_prefill_bf16_T8192_W4096_D128_gqa": ("window_prefill", "roofline", "avg_launch_us"),
+        "varlen_prefill_bf16_32K_tokens_D128_gqa": ("varlen_prefill", "roofline", "avg_launch_us"),
+        "prefill_bf16_gpt2s_B4_H12_T1024_D64": ("small_prefill", "gpt2s_causal_bf16_B4_H12_T1024_D64",
+                                                "roofline", "avg_launch_us"),
+        "decode_split_bf16_B4_T32768_D128": ("long_decode", "roofline", "avg_call_us"),
+        "decode_combine_bf16_B4_T32768_D128": ("long_decode", "roofline", "avg_call_us"),
+    }.get(name)
+    d = line
+    for k in path or ():
+        if not isinstance(d, dict) or k not in d:
+            return None
+        d = d[k]
+    return d if isinstance(d, (int, float)) else None
+
+
+def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note, names=None, n_timed=20):
     """Turn rocprofv3 CSV output (a --kernel-trace --stats run and two --pmc
     runs, FETCH_SIZE then WRITE_SIZE, each with a device copy of copy_mib MiB
-    for calibration) into the summaries kept under profiles/."""
+    for calibration) into the summaries kept under profiles/.  Durations are
+    reported over all dispatches and over the last n_timed (the bench's timed
+    calls, after its warm-up)."""
     import glob
     stats = _csv_rows(glob.glob(f"{trace_dir}/**/*kernel_stats.csv", recursive=True)[0])
 
@@ -192,12 +302,17 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note, names=Non
         fetch_b = fk * 1024.0 * f_scale
         write_b = wk * 1024.0 * w_scale
         digest = source_digest([csrc / f for f in files])
+        timed = timed_dispatches(trace_dir, sub, n_timed)
+        tsorted = sorted(timed)
         rec = {
             "kernel": st["Name"],
             "source_sha256": digest,
             "calls": int(st["Calls"]),
             "avg_duration_us": round(float(st["AverageNs"]) / 1e3, 2),
             "min_duration_us": round(float(st["MinNs"]) / 1e3, 2),
+            "timed_dispatches": len(timed),
+            "avg_timed_us": round(sum(timed) / max(len(timed), 1), 2),
+            "median_timed_us": round(tsorted[len(tsorted) // 2], 2) if timed else None,
             "fetch_size_kib_raw": fk,
             "write_size_kib_raw": wk,
             "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib_raw": f_copy,
@@ -208,13 +323,19 @@ def summarize(trace_dir, fetch_dir, write_dir, copy_mib, command_note, names=Non
             "hbm_bytes_per_launch": round(fetch_b + write_b),
             "algorithmic_bytes_per_launch": algo[name],
         }
+        ev = bench_event_us(bench_line_from_log(f"{trace_dir}.log"), name)
+        if ev is not None:
+            rec["bench_event_avg_us_same_run"] = ev
         (PROFILES / f"{name}_traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
         md = [f"# {name}", "", f"Kernel: `{st['Name']}`", "",
               "Commands (from the repository root on the GPU host):", "", "```", command_note, "```", "",
               "| figure | value |", "|---|---|",
               f"| dispatches | {rec['calls']} |",
-              f"| average duration (kernel trace) | {rec['avg_duration_us']} us |",
+              f"| average duration (kernel trace, all dispatches incl. warm-up) | {rec['avg_duration_us']} us |",
+              f"| average / median of the last {rec['timed_dispatches']} dispatches (the bench's timed calls) | "
+              f"{rec['avg_timed_us']} / {rec['median_timed_us']} us |",
               f"| minimum duration | {rec['min_duration_us']} us |",
+              *([f"| the bench's own HIP-event average in the same run | {ev} us |"] if ev is not None else []),
               f"| FETCH_SIZE raw / dispatch | {fk:.0f} KiB |",
               f"| WRITE_SIZE raw / dispatch | {wk:.0f} KiB |",
               f"| copy calibration ({copy_mib} MiB read + written) | FETCH x{f_scale:.3f}, WRITE x{w_scale:.3f} |",
@@ -269,6 +390,13 @@ def summarize_counters(dirs, command_note, name="prefill_bf16_T8192_D128_gqa"):
           "| derived | value |", "|---|---|", *derived, "",
           "| counter (sum over instances, average per dispatch) | value |", "|---|---|", *rows, ""]
     (PROFILES / f"{name}_counters.md").write_text("\n".join(md))
+    files = KERNELS[name][1]
+    csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
+    (PROFILES / f"{name}_counters.json").write_text(json.dumps({
+        "kernel": sub, "source_sha256": source_digest([csrc / f for f in files]),
+        "dispatches_sampled": len(gui), "shader_cycles_per_launch": round(cyc),
+        "shader_clock_ghz": round(ghz, 3), "counters_per_dispatch": {c: avg[c] for c in sorted(avg)},
+    }, indent=1) + "\n")
     print(f"wrote profiles/{name}_counters.md")
 
 
@@ -281,6 +409,7 @@ def profile_traffic(name):
     _, files = KERNELS[name]
     csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
     return traffic_from_profile(name, source_digest([csrc / f for f in files]))
+LONG_DECODE = (4, 32, 8, 32768, 128, 16)  # B, H_q, H_kv, T_kv, D, default split count
 WINDOW = 4096                 # sliding-window line: Mistral-style 4K window
 VARLEN_TOKENS = 32768         # packed-batch line: total query tokens
 
@@ -471,10 +600,165 @@ def qkv_projection_line(abi, torch, np, stream, dev, warmup, settle, steps):
     return line
 
 
+def small_prefill_lines(abi, torch, np, stream, dev, warmup, settle, steps):
+    """The three small workloads: B1 H1 T128 D64 fp32 non-causal, B1 H4 T128
+    D64 bf16 causal, and the GPT-2-small shape B4 H12 T1024 D64 bf16 causal.
+    Each is timed per call (the first two are launch-latency bound)."""
+    from transformer_scaled_dot_flash_amd.workloads import BY_ORDINAL
+    out = {}
+    for ordinal in (1, 2, 3):
+        w = BY_ORDINAL[ordinal]
+        q, k, v = w.make_inputs()
+        if w.dtype == "bf16":
+            qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+        else:
+            qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        od = torch.empty_like(qd)
+        code = abi.ATTN_BF16 if w.dtype == "bf16" else abi.ATTN_F32
+
+        def run():
+            abi.attn_fwd_prefill(qd, kd, vd, od, w.B, w.H_q, w.H_kv, w.T_q, w.T_kv, w.D, w.causal, w.scale,
+                                 code, stream)
+        log(f"small prefill {w.name}")
+        avg, mn = time_calls(torch, stream, run, max(warmup, 20), settle, max(steps, 50))
+        tf = w.flops() / (avg * 1e-3) / 1e12
+        peak = PEAK_F32_VALU_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        line = {"metric": "prefill call latency (us) and TFLOP/s", "value": round(avg * 1e3, 2), "unit": "us",
+                "tflops": round(tf, 2),
+                "config": {"workload": w.name, "flops": w.flops(), "bytes": w.bytes()},
+                "roofline": {"bound": "alu" if w.dtype == "f32" else "mfma",
+                             "kernel": "attn_f32_kernel<64>" if w.dtype == "f32" else "prefill_bf16_kernel<D=64,causal,BN=64,4 waves>",
+                             "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                             "frac": round(tf / peak, 5), "traffic": None,
+                             "avg_launch_us": round(avg * 1e3, 2), "min_launch_us": round(mn * 1e3, 2)}}
+        if ordinal == 3:
+            line["roofline"]["traffic"] = profile_traffic("prefill_bf16_gpt2s_B4_H12_T1024_D64")
+        out[w.name] = line
+    return out
+
+
+def long_decode_line(abi, torch, np, stream, dev, warmup, settle, steps):
+    """Long-context decode whose default plan splits the keys: B=4 H_q=32
+    H_kv=8 T_kv=32768 D=128 bf16 (32 (batch, kv head) groups, 16 splits):
+    the split pass writes per-split partials, the combine pass merges them."""
+    from transformer_scaled_dot_flash_amd import inputs
+    B, H_q, H_kv, T, D, S_expect = LONG_DECODE
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+
+    def mk(seed, shape):
+        bits = inputs.normal(seed, shape, "bf16")
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev), bits
+    (q, qb), (k, kb), (v, vb) = mk(9001, (B, H_q, 1, D)), mk(9002, (B, H_kv, T, D)), mk(9003, (B, H_kv, T, D))
+    o = torch.empty_like(q)
+    splits = abi.attn_fwd_decode_default_splits(B, H_q, H_kv, T, D)
+    ws_bytes = abi.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T, D, abi.ATTN_BF16, 0)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def run():
+        abi.attn_fwd_decode(q, k, v, o, B, H_q, H_kv, 1, T, D, False, scale, abi.ATTN_BF16, 0, ws, ws_bytes, stream)
+    log(f"long decode B={B} T_kv={T} ({splits} splits)")
+    avg, mn = time_calls(torch, stream, run, warmup, settle, max(steps, 50))
+    kv_bytes = 2 * 2 * B * H_kv * T * D
+    nbytes = kv_bytes + 2 * 2 * B * H_q * D
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    part_bytes = 2 * B * H_q * splits * (D + 2) * 4  # partials written by the split pass, read by the combine
+    line = {"metric": "long-context decode KV-read GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "config": {"workload": f"decode B={B} H_q={H_q} H_kv={H_kv} T_kv={T} D={D} bf16", "splits": splits,
+                       "bytes": nbytes, "partials_bytes": part_bytes,
+                       "partials_share_of_bytes": round(part_bytes / nbytes, 5)},
+            "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "avg_call_us": round(avg * 1e3, 2), "min_call_us": round(mn * 1e3, 2)}}
+    sp = profile_record("decode_split_bf16_B4_T32768_D128")
+    cb = profile_record("decode_combine_bf16_B4_T32768_D128")
+    if sp and cb:
+        line["roofline"]["traffic"] = sp["hbm_bytes_per_launch"] + cb["hbm_bytes_per_launch"]
+        line["combine_share_of_time"] = round(cb["avg_timed_us"] / (sp["avg_timed_us"] + cb["avg_timed_us"]), 4)
+        line["split_kernel_us"] = sp["avg_timed_us"]
+        line["combine_kernel_us"] = cb["avg_timed_us"]
+    # parity of this call against the oracle (every element)
+    import oracle
+    torch.cuda.synchronize()
+    got = inputs.bf16_bits_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    want = oracle.attention(inputs.as_f64(qb, "bf16"), inputs.as_f64(kb, "bf16"), inputs.as_f64(vb, "bf16"),
+                            scale, False)
+    line["parity"] = parity_stats(got, want)
+    return line
+
+
+def profile_record(name):
+    """profiles/<name>_traffic.json when it belongs to the current source."""
+    f = PROFILES / f"{name}_traffic.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    _, files = KERNELS[name]
+    csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
+    return d if d.get("source_sha256") == source_digest([csrc / f_ for f_ in files]) else None
+
+
+def ceilings(torch, stream, dev, run_prefill=None):
+    """Measured ceilings beside the published peaks: a register-fed bf16 MFMA
+    loop (TFLOP/s and its shader clock), a 1 GiB streaming read (GB/s, the
+    decode kernel's load pattern), and the shader clock sampled while the
+    prefill runs."""
+    from transformer_scaled_dot_flash_amd import probe
+    probe.load_library()
+    n_wg, iters = 1024, 4000
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(n_wg * 8 * 2, dtype=torch.int64, device=dev)
+    for _ in range(3):  # warm-up, then the timed launch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        probe.attn_probe_mfma(n_wg, iters, out, cyc, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = n_wg * 8 * iters * 4 * 32768
+    c = cyc.view(-1, 2).double()
+    mfma_clock = float((c[:, 0] / (c[:, 1] * 10.0)).median())  # reference clock: 100 MHz
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    times = []
+    for i in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        probe.attn_probe_stream_read(src, nbytes, sink, 4096, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1))
+    res = {"mfma_bf16_tflops": round(flops / (ms * 1e-3) / 1e12, 1), "mfma_clock_ghz": round(mfma_clock, 3),
+           "stream_read_gbs": round(nbytes / (sorted(times)[len(times) // 2] * 1e-3) / 1e9, 1),
+           "published_bf16_tflops": PEAK_BF16_TFLOPS, "published_hbm_gbs": PEAK_HBM_GBS,
+           "published_clock_ghz": 2.4}
+    del src
+    if run_prefill is not None:
+        # clock while the prefill runs: a one-wave sampler on a second stream
+        # (default priority) shares a CU with the prefill's workgroups
+        side = torch.cuda.Stream(device=dev)
+        clk = torch.zeros(2, dtype=torch.int64, device=dev)
+        samples = []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            run_prefill()
+            run_prefill()
+            with torch.cuda.stream(side):
+                probe.attn_probe_clock(clk, 20000, side)  # 200 us of reference ticks
+            torch.cuda.synchronize()
+            samples.append(float(clk[0]) / (float(clk[1]) * 10.0))
+        res["prefill_clock_ghz"] = round(sorted(samples)[len(samples) // 2], 3)
+    return res
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
-        # python bench.py --summarize-counters "commands" DIR [DIR ...]
-        summarize_counters(sys.argv[3:], sys.argv[2])
+        # python bench.py --summarize-counters "commands" DIR DIR [NAME]
+        names = [a for a in sys.argv[3:] if a in KERNELS]
+        dirs = [a for a in sys.argv[3:] if a not in KERNELS]
+        summarize_counters(dirs, sys.argv[2], *(names[:1]))
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         # python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR COPY_MIB "commands" [NAME ...]
@@ -487,11 +771,16 @@ def main():
     ap.add_argument("--settle", type=float, default=1.0,
                     help="minimum seconds of untimed warm-up (GPU clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "paged", "window", "varlen", "qkv"],
+    ap.add_argument("--only", choices=["prefill", "decode", "paged", "window", "varlen", "qkv", "small",
+                                       "long_decode", "ceilings"],
                     default=None, help="time one part only (for profiling runs)")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV decode line")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the sliding-window, packed-batch and QKV-projection lines")
+                    help="skip the sliding-window, packed-batch, QKV-projection, small-workload "
+                         "and long-decode lines")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle comparison of the decode workload's output")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -590,6 +879,15 @@ def main():
     if all_extra or args.only == "qkv":
         extra["qkv_projection"] = qkv_projection_line(abi, torch, np, stream, dev, args.warmup,
                                                       args.settle, min(K, 20))
+    if all_extra or args.only == "small":
+        extra["small_prefill"] = small_prefill_lines(abi, torch, np, stream, dev, args.warmup,
+                                                     args.settle, min(K, 20))
+    if all_extra or args.only == "long_decode":
+        extra["long_decode"] = long_decode_line(abi, torch, np, stream, dev, args.warmup, args.settle,
+                                                min(K, 20))
+    if (args.only is None and not args.no_ceilings) or args.only == "ceilings":
+        log("measured ceilings")
+        extra["ceilings"] = ceilings(torch, stream, dev, run_prefill if args.only is None else None)
     paged = None
     if do_pg:
         paged = time_paged_decode(abi, torch, wd, kd, vd, qd, od if do_d else None, stream, dev,
@@ -664,9 +962,30 @@ def main():
     if paged is not None:
         result["paged_decode"] = paged
     result.update(extra)
+    parity = {}
+    if do_d and not args.no_parity:
+        # the decode workload's output of the timed calls, every element against the oracle
+        import oracle
+        from transformer_scaled_dot_flash_amd import inputs
+        log("decode parity (oracle)")
+        qb, kb, vb = wd.make_inputs()
+        want = oracle.attention(*(inputs.as_f64(x, "bf16") for x in (qb, kb, vb)), wd.scale, False)
+        got = inputs.bf16_bits_to_f32(od.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        parity["decode"] = parity_stats(got, want)
     if not args.no_cpu_baseline and do_p:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline()
+        rec, heads = cpu_baseline()
+        rec["gpu_over_oracle"] = round(p_tflops / rec["value"], 1) if rec["value"] else None
+        result["cpu_baseline"] = rec
+        # the prefill output of the timed calls against the oracle heads just computed
+        from transformer_scaled_dot_flash_amd import inputs
+        hs = sorted(heads)
+        got = inputs.bf16_bits_to_f32(op[0, hs].view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        want = np.stack([heads[h] for h in hs])
+        parity["prefill"] = parity_stats(got, want)
+        parity["prefill"]["heads_compared"] = f"{len(hs)} of {wp.H_q} q heads, every row and feature"
+    if parity:
+        result["parity"] = parity
     print(json.dumps(result), flush=True)
 
 

@@ -300,3 +300,27 @@ def test_qkv_rejects(kw, want):
 def test_qkv_empty_ok():
     assert qkv(B=0, x=0, w=0, q=0, k=0, v=0) == OK
     assert qkv(T=0, x=0, w=0, q=0, k=0, v=0) == OK
+
+
+# --- measurement probe library ------------------------------------------------------
+def test_probe_library_exports_its_header():
+    from transformer_scaled_dot_flash_amd import probe
+    text = re.sub(r"/\*.*?\*/", "", (ROOT / "include" / "attn_probe.h").read_text(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(attn_probe_[a-z0-9_]+)\s*\(", text)))
+    assert set(declared) == set(probe.EXPORTED)
+    lib = ctypes.CDLL(str(probe.LIB_PATH))
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_probe_rejects_bad_arguments_before_launching():
+    from transformer_scaled_dot_flash_amd import probe
+    lib = probe.load_library()
+    inval = 1  # hipErrorInvalidValue
+    assert lib.attn_probe_mfma(0, 10, 0x1000, 0x2000, None) == inval
+    assert lib.attn_probe_mfma(4, 10, None, 0x2000, None) == inval
+    assert lib.attn_probe_stream_read(0x1000, 1 << 20, 0x2000, 3, None) == inval   # not a 64 KiB multiple per WG
+    assert lib.attn_probe_stream_read(0x1000, 0, 0x2000, 4, None) == inval
+    assert lib.attn_probe_stream_read(None, 1 << 26, 0x2000, 4, None) == inval
+    assert lib.attn_probe_clock(None, 100, None) == inval
+    assert lib.attn_probe_clock(0x1000, 0, None) == inval

@@ -3,6 +3,8 @@
 * ``_lib/libattn.so``      the HIP kernels for gfx950 and the C ABI
                            (``include/attn.h``), built with hipcc.
 * ``_lib/libattn_gen.so``  the seeded input generator (plain C, gcc).
+* ``_lib/libattn_probe.so`` measurement kernels of the benchmark (measured
+                           ceilings and shader clock, ``include/attn_probe.h``).
 
 Both are always rebuilt when :func:`build_all` is called.  Loading code never
 builds: it raises if a library is missing.
@@ -34,7 +36,7 @@ HIP_SOURCES = [
     CSRC / "decode_bf16.hip",
     CSRC / "qkv_bf16.hip",
 ]
-HIP_HEADERS = [CSRC / "kernel_common.h", INCLUDE / "attn.h"]
+HIP_HEADERS = [CSRC / "kernel_common.h", INCLUDE / "attn.h", INCLUDE / "attn_probe.h"]
 
 # gfx950 only.  Packed fp32 VALU ops are switched off for all device code.
 HIP_FLAGS = [
@@ -98,9 +100,19 @@ def build_hip(jobs: int = 4) -> Path:
     return out
 
 
+def build_probe() -> Path:
+    LIBDIR.mkdir(exist_ok=True)
+    out = LIBDIR / "libattn_probe.so"
+    tmp = out.with_suffix(".so.tmp")
+    _run([_hipcc(), *HIP_FLAGS, "-shared", "-I", str(INCLUDE), str(CSRC / "probe" / "ceilings.hip"), "-o", str(tmp)])
+    os.replace(tmp, out)
+    return out
+
+
 def build_all() -> None:
     build_gen()
     build_hip()
+    build_probe()
 
 
 if __name__ == "__main__":
