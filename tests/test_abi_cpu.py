@@ -109,22 +109,29 @@ def test_decode_empty_batch_ok():
     assert decode(B=0, q=0, k=0, v=0, o=0, ws=0, ws_bytes=0) == OK
 
 
+def ws_expected(B, H_q, H_kv, S, D):
+    """(D + 2) fp32 values per (batch, q head, split); 0 for one split."""
+    if S <= 1:
+        return 0
+    return B * H_q * S * (D + 2) * 4
+
+
 def test_decode_workspace_size():
-    # (D + 2) fp32 values per (batch, q head, split)
     B, H_q, H_kv, T_kv, D = 64, 32, 8, 4096, 128
     n = A.attn_fwd_decode_default_splits(B, H_q, H_kv, T_kv, D)
     assert n == 1  # 512 (batch, kv head) groups fill the GPU: no split, no workspace
     assert A.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, BF16, 0) == 0
     for req, eff in [(1, 0), (8, 8), (64, 64), (128, 128), (4096, 0)]:
         got = A.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, BF16, req)
-        assert got == B * H_q * eff * (D + 2) * 4  # 0 for one split or an out-of-range request
+        assert got == ws_expected(B, H_q, H_kv, eff, D)  # 0 for one split or an out-of-range request
     # few groups: the keys are split to fill the GPU
     assert A.attn_fwd_decode_default_splits(1, 32, 8, 4096, 128) == 32
     # split count is clamped to the number of 32-key blocks and never leaves a split empty
-    assert A.attn_fwd_decode_workspace_bytes(1, 4, 1, 100, 64, BF16, 64) == 1 * 4 * 4 * 66 * 4
-    assert A.attn_fwd_decode_workspace_bytes(1, 4, 1, 100, 64, BF16, 3) == 1 * 4 * 2 * 66 * 4
+    assert A.attn_fwd_decode_workspace_bytes(1, 4, 1, 100, 64, BF16, 64) == ws_expected(1, 4, 1, 4, 64)
+    assert A.attn_fwd_decode_workspace_bytes(1, 4, 1, 100, 64, BF16, 3) == ws_expected(1, 4, 1, 2, 64)
     assert A.attn_fwd_decode_workspace_bytes(1, 4, 1, 100, 64, F32, 0) == 0
     assert A.attn_fwd_decode_workspace_bytes(1, 4, 3, 100, 64, BF16, 0) == 0
+    assert A.attn_fwd_decode_workspace_bytes(1, 64, 1, 4096, 128, BF16, 8) == ws_expected(1, 64, 1, 8, 128)
 
 
 def test_decode_workspace_too_small_by_one_byte():
@@ -157,10 +164,9 @@ def test_decode_noalloc_scratch_limit_is_exact():
     # the largest plan that fits is accepted by validation (checked on an
     # empty batch: nothing launched); one split more needs too much
     B, H_q, H_kv, T_kv, D = 4, 32, 8, 1 << 20, 128
-    per_split = B * H_q * (D + 2) * 4
-    fits = SCRATCH_BYTES // per_split
-    assert A.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, BF16, fits) <= SCRATCH_BYTES
-    assert A.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, BF16, fits + 1) > SCRATCH_BYTES
+    sizes = {S: A.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T_kv, D, BF16, S) for S in range(2, 1025)}
+    fits = max(S for S, n in sizes.items() if n <= SCRATCH_BYTES)
+    assert sizes[fits] <= SCRATCH_BYTES < sizes[fits + 1]
     far = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40)  # 1 GiB K and V: well apart
     assert decode_noalloc(B=B, H_q=H_q, H_kv=H_kv, T_kv=T_kv, splits=fits + 1, **far) == SCRATCH
     assert decode_noalloc(B=0, H_q=H_q, H_kv=H_kv, T_kv=T_kv, splits=fits, q=0, k=0, v=0, o=0) == OK
@@ -220,7 +226,7 @@ def test_paged_workspace_size():
     # one split (enough groups) -> no workspace; few groups -> split over max_pages * ps keys
     assert A.attn_fwd_decode_paged_workspace_bytes(64, 32, 8, 128, 16, 256, 0) == 0
     n = A.attn_fwd_decode_paged_workspace_bytes(1, 32, 8, 128, 16, 256, 0)
-    assert n == 1 * 32 * A.attn_fwd_decode_default_splits(1, 32, 8, 4096, 128) * 130 * 4
+    assert n == ws_expected(1, 32, 8, A.attn_fwd_decode_default_splits(1, 32, 8, 4096, 128), 128)
     assert A.attn_fwd_decode_paged_workspace_bytes(2, 8, 2, 128, 16, 8, 4) == \
         A.attn_fwd_decode_workspace_bytes(2, 8, 2, 128, 128, BF16, 4)
     assert A.attn_fwd_decode_paged_workspace_bytes(2, 8, 2, 128, 12, 8, 4) == 0  # bad page size

@@ -389,3 +389,47 @@ def test_library_loaded_before_torch_in_a_fresh_process():
     ) % (str(root), str(root / "tests"))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "ok" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
+
+
+def test_decode_split_merge_with_reused_workspace():
+    """One workspace, first filled with 0xFF bytes, serves five split decodes
+    (16 splits) on different inputs: every output matches the oracle and a
+    fresh-workspace call bit for bit (nothing is carried over between
+    calls)."""
+    import torch
+    B, H_q, H_kv, T, D = 4, 32, 8, 3000, 128
+    assert abi.attn_fwd_decode_default_splits(B, H_q, H_kv, T, D) == 16
+    nbytes = abi.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T, D, abi.ATTN_BF16, 0)
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    for i in range(5):
+        q = gen(700 + 3 * i, (B, H_q, 1, D), "bf16")
+        k = gen(701 + 3 * i, (B, H_kv, T, D), "bf16")
+        v = gen(702 + 3 * i, (B, H_kv, T, D), "bf16")
+        qd, kd, vd = (G.to_device(x, "bf16") for x in (q, k, v))
+        o = torch.empty_like(qd)
+        G.note(f"decode with a reused workspace, call {i}")
+        abi.attn_fwd_decode(qd, kd, vd, o, B, H_q, H_kv, 1, T, D, False, scale, abi.ATTN_BF16, 0, ws, nbytes,
+                            torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        got = G.to_f64(o, "bf16")
+        fresh = G.decode(q, k, v, scale, "bf16")
+        assert np.array_equal(got, fresh)
+        want = oracle.attention(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), scale, False)
+        assert G.max_err(got, want) <= G.TOL["bf16"]
+
+
+@pytest.mark.parametrize("H_q,H_kv,splits", [(8, 2, 16), (4, 4, 2), (3, 3, 5), (16, 4, 7), (12, 3, 16),
+                                             (5, 5, 17), (40, 8, 9)])
+def test_decode_split_counts_match_oracle(H_q, H_kv, splits):
+    """Split decodes over a range of split counts and group sizes, D = 64 and
+    128."""
+    for D in (64, 128):
+        B, T = 3, 1111
+        q = gen(810 + D, (B, H_q, 1, D), "bf16")
+        k = gen(811 + D, (B, H_kv, T, D), "bf16")
+        v = gen(812 + D, (B, H_kv, T, D), "bf16")
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        got = G.decode(q, k, v, scale, "bf16", splits)
+        want = oracle.attention(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), scale, False)
+        assert G.max_err(got, want) <= G.TOL["bf16"], (H_q, H_kv, splits, D)

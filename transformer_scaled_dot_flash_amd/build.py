@@ -36,7 +36,7 @@ HIP_SOURCES = [
     CSRC / "decode_bf16.hip",
     CSRC / "qkv_bf16.hip",
 ]
-HIP_HEADERS = [CSRC / "kernel_common.h", INCLUDE / "attn.h", INCLUDE / "attn_probe.h"]
+HIP_HEADERS = [CSRC / "kernel_common.h", CSRC / "launch.h", INCLUDE / "attn.h", INCLUDE / "attn_probe.h"]
 
 # gfx950 only.  Packed fp32 VALU ops are switched off for all device code.
 HIP_FLAGS = [

@@ -7,7 +7,7 @@
 #include <mutex>
 
 #include "attn.h"
-#include "kernel_common.h"
+#include "launch.h"
 
 namespace {
 
@@ -106,6 +106,8 @@ SplitPlan plan_splits(int B, int H_q, int H_kv, int T_kv, int requested) {
     return p;
 }
 
+// Workspace of a split plan: partial outputs [B][H_q][S][D] fp32, then
+// (max, sum) [B][H_q][S][2] fp32.
 size_t decode_ws_bytes(int B, int H_q, int D, const SplitPlan& p) {
     if (p.n_splits == 1) return 0;  // the split pass writes O directly
     return (size_t)B * H_q * p.n_splits * (D + 2) * sizeof(float);
@@ -136,6 +138,12 @@ attn_status_t check_paged_params(int B, int H_q, int H_kv, int D, int page_size,
     return ATTN_OK;
 }
 
+// Workspace pointers of a decode launch (partial outputs, then (max, sum)).
+void set_workspace(attn::DecodeArgs& a, void* ws, int B, int H_q, int D, const SplitPlan& p) {
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_ml = ws ? a.ws_o + (size_t)B * H_q * p.n_splits * D : nullptr;
+}
+
 // The bf16 decode launch shared by attn_fwd_decode and
 // attn_fwd_decode_noalloc: `ws` holds the split partials (unused with one
 // split).
@@ -155,8 +163,7 @@ attn_status_t decode_bf16(const void* q, const void* k, const void* v, void* o, 
     positive_scale(scale, &a.c_log2, &a.neg_q);
     a.n_splits = p.n_splits;
     a.keys_per_split = p.keys_per_split;
-    a.ws_o = static_cast<float*>(ws);
-    a.ws_ml = ws ? a.ws_o + (size_t)B * H_q * p.n_splits * D : nullptr;
+    set_workspace(a, ws, B, H_q, D, p);
     return hip_status(attn::launch_decode_bf16(a, s));
 }
 
@@ -464,8 +471,7 @@ attn_status_t attn_fwd_decode_paged(const void* q, const void* k_pages, const vo
     positive_scale(scale, &a.c_log2, &a.neg_q);
     a.n_splits = p.n_splits;
     a.keys_per_split = p.keys_per_split;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = a.ws_o + (size_t)B * H_q * p.n_splits * D;
+    set_workspace(a, need > 0 ? workspace : nullptr, B, H_q, D, p);
     a.paged.block_table = block_table;
     a.paged.seq_lens = seq_lens;
     a.paged.max_pages = max_pages;

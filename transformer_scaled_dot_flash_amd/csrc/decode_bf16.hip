@@ -38,7 +38,7 @@
 // size, rows past the sequence's length read as zero, and a block id outside
 // the pool reads as a page of zeros instead of faulting).  The block ids of
 // 64 consecutive pages are held one per lane and picked with v_readlane.
-#include "kernel_common.h"
+#include "launch.h"
 
 namespace attn {
 namespace {
@@ -301,31 +301,83 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     }
 }
 
-// One wave per (batch, q head): merge the split states and write O.
+// One wave per (batch, q head): merge the split states and write O.  Lane
+// (split group sg = lane / 16, feature group fq = lane % 16) merges splits
+// sg, sg + 4, sg + 8, ... for features fq * D/16 ... with the online form of
+// the merge rule (running base, sum and output), four splits' loads in
+// flight at a time; the four split groups are then merged across lanes
+// (two exchanges) and the first group writes O.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws_o,
                                                             const float* __restrict__ ws_ml,
                                                             bf16* __restrict__ O, int n_splits) {
+    constexpr int FPL = D / 16;  // features per lane
     const size_t row = blockIdx.x;
     const int lane = threadIdx.x;
+    const int sg = lane >> 4, fq = lane & 15;
     const float* ml = ws_ml + row * n_splits * 2;
-    float m = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) m = fmaxf(m, ml[2 * s]);
-    if (m == -INFINITY) m = 0.f;  // every split empty (a paged sequence of length 0): O = 0
-    float L = 0.f;
-    float acc[D / 64];
+    const float* op = ws_o + row * n_splits * D + fq * FPL;
+    float m = -INFINITY, L = 0.f, acc[FPL];
 #pragma unroll
-    for (int r = 0; r < D / 64; ++r) acc[r] = 0.f;
-    const float* op = ws_o + row * n_splits * D + lane;
-    for (int s = 0; s < n_splits; ++s) {
-        const float w = ml[2 * s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[2 * s] - m);
-        L += ml[2 * s + 1] * w;
+    for (int f = 0; f < FPL; ++f) acc[f] = 0.f;
+    // merge one split state (ms, ls, o) into (m, L, acc)
+    auto merge = [&](float ms, float ls, const f32x4 (&o)[FPL / 4]) {
+        if (ms == -INFINITY) return;  // an empty split (paged sequence shorter than the split start)
+        const float mn = fmaxf(m, ms);
+        const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        const float w = __builtin_amdgcn_exp2f(ms - mn);
+        L = L * a + ls * w;
 #pragma unroll
-        for (int r = 0; r < D / 64; ++r) acc[r] += w * op[(size_t)s * D + 64 * r];
+        for (int f = 0; f < FPL; ++f) acc[f] = acc[f] * a + o[f / 4][f % 4] * w;
+        m = mn;
+    };
+    constexpr int U = 4;  // splits per lane in flight
+    for (int s0 = sg; s0 < n_splits; s0 += 4 * U) {
+        float ms[U], ls[U];
+        f32x4 o[U][FPL / 4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int sp = s0 + 4 * u;
+            ms[u] = -INFINITY;
+            ls[u] = 0.f;
+            if (sp < n_splits) {
+                ms[u] = ml[2 * sp];
+                ls[u] = ml[2 * sp + 1];
+#pragma unroll
+                for (int c = 0; c < FPL / 4; ++c) o[u][c] = *reinterpret_cast<const f32x4*>(op + (size_t)sp * D + 4 * c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) merge(ms[u], ls[u], o[u]);
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    // merge the four split groups: lanes lane ^ 16, then lane ^ 32
 #pragma unroll
-    for (int r = 0; r < D / 64; ++r) O[row * D + lane + 64 * r] = (bf16)(acc[r] * inv);
+    for (int x = 16; x <= 32; x <<= 1) {
+        const float m2 = __shfl_xor(m, x), L2 = __shfl_xor(L, x);
+        f32x4 o2[FPL / 4];
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) o2[f / 4][f % 4] = __shfl_xor(acc[f], x);
+        // rescale so (m2, L2, o2) is a merged state, then merge it
+        const float mn = fmaxf(m, m2);
+        const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        const float b = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+        L = L * a + L2 * b;
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) acc[f] = acc[f] * a + o2[f / 4][f % 4] * b;
+        m = mn;
+    }
+    if (sg == 0) {
+        // every split empty (a paged sequence of length 0): L = 0, O = 0
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        bf16* orow = O + row * D + fq * FPL;
+#pragma unroll
+        for (int g4 = 0; g4 < FPL / 4; ++g4) {
+            bf16x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = (bf16)(acc[4 * g4 + q] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 4 * g4) = w;
+        }
+    }
 }
 
 template <int D, bool PAGED>

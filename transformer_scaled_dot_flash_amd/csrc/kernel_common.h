@@ -216,23 +216,6 @@ __device__ inline void buf_store_b128(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_
 // factor into the score multiplier once on the host.
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 
-struct PrefillArgs {
-    const void* q;
-    const void* k;
-    const void* v;
-    void* o;
-    int B, H_q, H_kv, T_q, T_kv, D;
-    int causal;
-    float scale;       // multiplier of the raw dot product
-    float scale_log2;  // scale * log2(e), rounded to float
-    float c_log2;      // |scale| * log2(e), >= FLT_MIN (0 becomes FLT_MIN: same weights)
-    int neg_q;         // 1 when scale < 0: the kernels flip Q's sign instead
-    int window;        // causal sliding window in keys (0: none)
-    const int* cu_q;   // packed batch: [B + 1] row offsets of each sequence's
-    const int* cu_k;   //   queries / keys (nullptr: contiguous [B][H][T][D])
-    int total_q;       // packed batch: rows of q (picks the launch shape)
-};
-
 // Paged KV cache of the decode kernel (block_table == nullptr: contiguous).
 struct PagedKV {
     const int* block_table;  // [B][max_pages] physical page of each logical page
@@ -241,52 +224,5 @@ struct PagedKV {
     int page_shift;          // log2(page_size)
     int num_pages;           // pages in each pool
 };
-
-struct DecodeArgs {
-    const void* q;
-    const void* k;
-    const void* v;
-    void* o;
-    int B, H_q, H_kv, T_kv, D;
-    float c_log2;  // |scale| * log2(e), >= FLT_MIN
-    int neg_q;     // 1 when scale < 0 (Q's sign is flipped instead)
-    int n_splits;        // effective split count (no split is empty)
-    int keys_per_split;  // multiple of 32
-    float* ws_o;         // [B][H_q][n_splits][D]  unnormalised partial outputs
-    float* ws_ml;        // [B][H_q][n_splits][2]  (running max in log2 units, sum)
-    PagedKV paged;       // paged cache (T_kv = max_pages * page_size), or all zero
-};
-
-struct QkvArgs {
-    const void* x;   // [M][d_model]
-    const void* w;   // [N][d_model], N = (H_q + 2 H_kv) D
-    void* q;         // [B][H_q][T][D]
-    void* k;         // [B][H_kv][T][D]
-    void* v;         // [B][H_kv][T][D]
-    int M, N, d_model, T, H_q, H_kv, D;
-};
-
-// Launchers return the HIP status of the launch call itself.
-hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_qkv_bf16(const QkvArgs& a, hipStream_t s);
-
-template <typename Tup, size_t... I>
-inline void fill_ptrs(Tup& t, void** p, std::index_sequence<I...>) {
-    ((p[I] = static_cast<void*>(&std::get<I>(t))), ...);
-}
-
-// Launch a kernel and return the launch's own error code (no reliance on the
-// thread's sticky last-error state).
-template <typename... KArgs, typename... Args>
-inline hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem,
-                                hipStream_t s, Args... args) {
-    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
-    auto tup = std::make_tuple(static_cast<KArgs>(args)...);
-    void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
-    fill_ptrs(tup, ptrs, std::index_sequence_for<KArgs...>{});
-    return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, s);
-}
 
 }  // namespace attn

@@ -64,7 +64,7 @@
 // FLOP but needs more than 256 registers per lane, i.e. one wave per SIMD,
 // and was measured slower: a single wave cannot overlap its own softmax with
 // its MFMAs the way two waves of a SIMD overlap each other's.
-#include "kernel_common.h"
+#include "launch.h"
 
 namespace attn {
 namespace {

@@ -14,7 +14,7 @@
 // K and V tiles of 32 keys are staged in LDS.
 #include <math.h>
 
-#include "kernel_common.h"
+#include "launch.h"
 
 namespace attn {
 namespace {

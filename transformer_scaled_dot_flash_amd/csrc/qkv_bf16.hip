@@ -33,7 +33,7 @@
 //     so the X and W tiles it reads are shared through its own L2.
 //   * Tokens past B T and features past N read as zero (range-checked buffer
 //     resources) and are not stored.  d_model must be a multiple of 64.
-#include "kernel_common.h"
+#include "launch.h"
 
 namespace attn {
 namespace {
