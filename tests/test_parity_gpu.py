@@ -108,6 +108,11 @@ PREFILL_CASES = [
     (1, 2, 2, 50, 77, 128, False, "bf16"),       # non-causal T_q != T_kv
     (1, 2, 2, 300, 40, 64, False, "bf16"),       # more queries than keys
     (8, 16, 8, 64, 64, 128, True, "bf16"),       # 64 kv units: XCD placement path
+    (2, 32, 8, 1100, 1100, 64, True, "bf16"),    # grid too large for the key split: 4-wave shape
+    (1, 32, 8, 1100, 1100, 128, True, "bf16"),   # the same at D = 128
+    (1, 8, 2, 1000, 1000, 64, True, "bf16"),     # key split, odd number of key tiles per group
+    (1, 4, 4, 130, 2000, 128, True, "bf16"),     # key split, chunk of queries at the end of the keys
+    (1, 2, 1, 200, 200, 128, False, "bf16"),     # key split, non-causal
     (1, 1, 1, 128, 128, 64, False, "f32"),
     (1, 1, 1, 1, 1, 64, True, "f32"),
     (2, 4, 2, 100, 100, 128, True, "f32"),

@@ -180,29 +180,39 @@ __device__ __attribute__((always_inline)) inline void score_tile(STile<BN, RB>& 
     score_groups<D, BN, RB, KOFF, KP>(st, f, a0, qf, std::make_integer_sequence<int, NM>{});
 }
 
-template <int D, bool CAUSAL, bool VARLEN, int RB, int BN, int WAVES, int WPE>
+// KSPLIT = 2 (short problems whose grid does not fill the GPU): the
+// workgroup's waves form two key groups over the same query rows; group g
+// walks the g-th half of the workgroup's key tiles with its own K/V ring, so
+// the longest chain of steps is halved, and at the end the second group's
+// (base, sum, unnormalised O) is merged into the first's through LDS with the
+// block-merge rule of AIInfraGuide section 12.3.
+template <int D, bool CAUSAL, bool VARLEN, int RB, int BN, int WAVES, int WPE, int KSPLIT = 1>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
 prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                     const bf16* __restrict__ V, bf16* __restrict__ O, int B, int H_q, int H_kv,
                     int T_q, int T_kv, int n_qt, float c, int neg_q, int window,
                     const int* __restrict__ cu_q, const int* __restrict__ cu_k) {
+    static_assert(KSPLIT == 1 || (KSPLIT == 2 && RB == 1), "key split: RB = 1");
+    constexpr int RW = WAVES / KSPLIT;            // waves per key group (row waves)
     constexpr int WROWS = 32 * RB;                // query rows per wave
-    constexpr int BM = WROWS * WAVES;             // query rows per workgroup
+    constexpr int BM = WROWS * RW;                // query rows per workgroup
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
     constexpr int ROWB = D * 2;                   // bytes per row
     constexpr int TILE = BN * ROWB;               // bytes of one K or V tile
-    constexpr int NLD = TILE / (1024 * WAVES);    // 1 KiB loads per wave per tile
-    static_assert(NLD * 1024 * WAVES == TILE, "tile must split into 1 KiB wave loads");
+    constexpr int NLD = TILE / (1024 * RW);       // 1 KiB loads per wave per tile
+    static_assert(NLD * 1024 * RW == TILE, "tile must split into 1 KiB wave loads");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];
-    unsigned char* const kring = smem;             // 2 K tiles
-    unsigned char* const vring = smem + 2 * TILE;  // 2 V tiles
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[KSPLIT * 4 * TILE];
 
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+    const int kg = KSPLIT > 1 ? wave_id / RW : 0;  // key group
+    const int wave = wave_id - kg * RW;            // row wave within the group
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
+    unsigned char* const kring = smem + kg * 4 * TILE;  // 2 K tiles of this key group
+    unsigned char* const vring = kring + 2 * TILE;      // 2 V tiles
 
     const TileCoord tc = map_tile(blockIdx.x, B, H_q, H_kv, n_qt, CAUSAL);
 
@@ -241,8 +251,13 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     // Key ranges: the workgroup's, this wave's, each row block's.
     const int last_row = min(T_q, q0 + BM) - 1;
     const int kv_end = CAUSAL ? max(0, min(T_kv, last_row + off + 1)) : T_kv;
-    const int n_kt = (kv_end + BN - 1) / BN;
-    const int t_lo = min(first_key(q0) / BN, n_kt);  // tiles left of every row's window are never visited
+    const int n_kt_wg = (kv_end + BN - 1) / BN;
+    const int t_lo_wg = min(first_key(q0) / BN, n_kt_wg);  // tiles left of every row's window are never visited
+    // This key group's tiles: [t_lo, n_kt), n_steps steps (the second group's
+    // last step may have no tile: n_kt - t_lo < n_steps).
+    const int n_steps = (n_kt_wg - t_lo_wg + KSPLIT - 1) / KSPLIT;
+    const int t_lo = t_lo_wg + kg * n_steps;
+    const int n_kt = min(n_kt_wg, t_lo + n_steps);
     int rb_kv_end[RB], rb_kv_begin[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -286,7 +301,8 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     auto issue_v = [&](int t) { issue(rV, vring + ((t - t_lo) & 1) * TILE, t); };
 
     // Prologue: K(t_lo), V(t_lo).  Step t issues K(t+1), V(t+1) into the
-    // slots of tile t-1, read for the last time in step t-1.
+    // slots of tile t-1, read for the last time in step t-1.  (Each key group
+    // loads its own tiles.)
     if (t_lo < n_kt) {
         issue_k(t_lo);
         issue_v(t_lo);
@@ -334,8 +350,9 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             }
         };
         if (!kIssueAfterScores) issue_next();
-        // Tiles above the diagonal or left of this wave's window: nothing to do.
-        if (!wave_live(j0)) {
+        // Tiles above the diagonal or left of this wave's window, or a key
+        // group's step past its last tile: nothing to do.
+        if (t >= n_kt || !wave_live(j0)) {
             if (kIssueAfterScores) issue_next();
             return;
         }
@@ -457,9 +474,42 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         pv_tile<D, BN / 16, RB>(oacc, pb, va);
         __builtin_amdgcn_s_setprio(0);
     };
-    for (int t = t_lo; t < n_kt; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < n_kt) step(t + 1, std::integral_constant<int, 1>{});
+    // Every key group runs n_steps steps (one barrier per step for all waves).
+    for (int i = 0; i < n_steps; i += 2) {
+        step(t_lo + i, std::integral_constant<int, 0>{});
+        if (i + 1 < n_steps) step(t_lo + i + 1, std::integral_constant<int, 1>{});
+    }
+
+    if constexpr (KSPLIT == 2) {
+        // Merge the second key group's state into the first's: per lane
+        // (D / 2 partial outputs, base, row sum) through LDS, now free.
+        constexpr int XS = D / 2 + 2;  // floats per lane
+        float* xch = reinterpret_cast<float*>(smem) + (size_t)(wave * 64 + lane) * XS;
+        const float l_mine = l_run[0] + swap_halves(l_run[0], xaddr);
+        __syncthreads();
+        if (kg == 1) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) xch[db * 16 + j] = oacc[0][db][j];
+            }
+            xch[D / 2] = m_use[0];
+            xch[D / 2 + 1] = l_mine;
+        }
+        __syncthreads();
+        if (kg == 1) return;
+        const float m_b = xch[D / 2], l_b = xch[D / 2 + 1];
+        const float m_a = m_use[0];
+        const float mm = fmaxf(m_a, m_b);
+        const float a = m_a == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_a - mm);
+        const float bw = m_b == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_b - mm);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[0][db][j] = oacc[0][db][j] * a + xch[db * 16 + j] * bw;
+        }
+        // the epilogue below adds the two halves of the row sum again
+        l_run[0] = l_mine * a * 0.5f + l_b * bw * 0.5f;
     }
 
     // Epilogue: O = O_acc / l, rounded once to bf16.  Rows past T_q fall
@@ -484,12 +534,12 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, int RB, int BN, int WAVES, int WPE>
+template <int D, bool CAUSAL, bool VARLEN, int RB, int BN, int WAVES, int WPE, int KSPLIT = 1>
 hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
-    constexpr int BM = 32 * RB * WAVES;
+    constexpr int BM = 32 * RB * WAVES / KSPLIT;
     const int n_qt = (a.T_q + BM - 1) / BM;
     const long long grid = (long long)a.B * a.H_q * n_qt;
-    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, VARLEN, RB, BN, WAVES, WPE>,
+    return launch_kernel(prefill_bf16_kernel<D, CAUSAL, VARLEN, RB, BN, WAVES, WPE, KSPLIT>,
                          dim3((unsigned)grid), dim3(64 * WAVES), 0, s, static_cast<const bf16*>(a.q),
                          static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                          static_cast<bf16*>(a.o), a.B, a.H_q, a.H_kv, a.T_q, a.T_kv, n_qt, a.c_log2,
@@ -509,6 +559,13 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t s) {
     const long long rows_per_seq = VARLEN ? a.total_q / (a.B > 0 ? a.B : 1) : a.T_q;
     const bool big = wg_big >= 512 && rows_per_seq >= 4096;
     if (big) return launch_cfg<D, CAUSAL, VARLEN, 1, 128, 8, 2>(a, s);
+    // Short problems whose 128-row workgroups all fit on the GPU at once
+    // (D = 64: 512 of them, two per CU; D = 128: 256): 8 waves in two key
+    // groups halve the longest chain of steps.  (A packed batch sizes the
+    // grid by its longest sequence, as dense problems by T_q.)
+    const long long wg4 = (long long)a.B * a.H_q * ((a.T_q + 127) / 128);
+    if (a.T_kv >= 128 && wg4 <= (D == 64 ? 512 : 256))
+        return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 8, D == 64 ? 4 : 2, 2>(a, s);
     return launch_cfg<D, CAUSAL, VARLEN, 1, 64, 4, 2>(a, s);
 }
 
