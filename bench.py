@@ -163,8 +163,8 @@ KERNELS = {
     # prefill<D=128, causal, packed, RB=1, BN=64, 4 waves>
     "varlen_prefill_bf16_32K_tokens_D128_gqa": ("prefill_bf16_kernelILi128ELb1ELb1ELi1ELi64ELi4E",
                                                 ["prefill_bf16.hip", "kernel_common.h"]),
-    # prefill<D=64, causal, contiguous, RB=1, BN=64, 4 waves>: the GPT-2-small workload
-    "prefill_bf16_gpt2s_B4_H12_T1024_D64": ("prefill_bf16_kernelILi64ELb1ELb0ELi1ELi64ELi4E",
+    # prefill<D=64, causal, contiguous, RB=1, BN=64, 8 waves, 4 per EU, 2 key groups>: the GPT-2-small workload
+    "prefill_bf16_gpt2s_B4_H12_T1024_D64": ("prefill_bf16_kernelILi64ELb1ELb0ELi1ELi64ELi8ELi4ELi2E",
                                             ["prefill_bf16.hip", "kernel_common.h"]),
     # long-context decode with split keys: split pass and combine pass
     "decode_split_bf16_B4_T32768_D128": ("decode_split_kernelILi128ELb0E", ["decode_bf16.hip", "kernel_common.h"]),
@@ -627,7 +627,7 @@ def small_prefill_lines(abi, torch, np, stream, dev, warmup, settle, steps):
                 "tflops": round(tf, 2),
                 "config": {"workload": w.name, "flops": w.flops(), "bytes": w.bytes()},
                 "roofline": {"bound": "alu" if w.dtype == "f32" else "mfma",
-                             "kernel": "attn_f32_kernel<64>" if w.dtype == "f32" else "prefill_bf16_kernel<D=64,causal,BN=64,4 waves>",
+                             "kernel": "attn_f32_kernel<64>" if w.dtype == "f32" else "prefill_bf16_kernel<D=64,causal,BN=64,8 waves in 2 key groups>",
                              "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                              "frac": round(tf / peak, 5), "traffic": None,
                              "avg_launch_us": round(avg * 1e3, 2), "min_launch_us": round(mn * 1e3, 2)}}
