@@ -5,8 +5,11 @@
 * ``_lib/libattn_gen.so``  the seeded input generator (plain C, gcc).
 * ``_lib/libattn_probe.so`` measurement kernels of the benchmark (measured
                            ceilings and shader clock, ``include/attn_probe.h``).
+* ``_lib/san/``            the C ABI and the generator again, with the host code
+                           built under AddressSanitizer and UndefinedBehavior-
+                           Sanitizer (CPU tests of the host-side validation).
 
-Both are always rebuilt when :func:`build_all` is called.  Loading code never
+All are rebuilt when :func:`build_all` is called.  Loading code never
 builds: it raises if a library is missing.
 """
 from __future__ import annotations
@@ -109,10 +112,64 @@ def build_probe() -> Path:
     return out
 
 
+# Host-side sanitizers only: on hipcc lines every flag goes to the host pass
+# (-Xarch_host), device code is built as usual (no GPU sanitizer).
+HIPCC_SAN_FLAGS = ["-Xarch_host", "-g",
+                   "-Xarch_host", "-fsanitize=address",
+                   "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=undefined",
+                   "-Xarch_host", "-fno-omit-frame-pointer"]
+# the generator is plain C, built by clang for the CPU only
+C_SAN_FLAGS = ["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+SANDIR = LIBDIR / "san"
+
+
+def asan_runtime() -> Path | None:
+    """The clang AddressSanitizer runtime matching hipcc's compiler."""
+    found = sorted(Path("/opt/rocm/llvm/lib/clang").glob("*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return found[-1] if found else None
+
+
+def build_sanitized(jobs: int = 5) -> Path:
+    """``_lib/san/libattn.so`` and ``_lib/san/libattn_gen.so`` with the host code
+    instrumented.  They are loaded only by a CPU test, in a child process that
+    preloads the sanitizer runtime."""
+    SANDIR.mkdir(parents=True, exist_ok=True)
+    hipcc = _hipcc()
+    host = HIPCC_SAN_FLAGS
+    objs, procs = [], []
+    for src in HIP_SOURCES:
+        obj = SANDIR / (src.stem + ".o")
+        objs.append(obj)
+        cmd = [hipcc, *HIP_FLAGS, *host, "-I", str(INCLUDE), "-I", str(CSRC), "-c", str(src), "-o", str(obj)]
+        print("[build]", " ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+        if len(procs) >= jobs:
+            if procs.pop(0).wait() != 0:
+                raise subprocess.CalledProcessError(1, "hipcc")
+    for p in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(1, "hipcc")
+    out = SANDIR / "libattn.so"
+    tmp = out.with_suffix(".so.tmp")
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *host, *map(str, objs), "-o", str(tmp)])
+    os.replace(tmp, out)
+    clang = Path(hipcc).resolve().parent.parent / "llvm" / "bin" / "clang"
+    if not clang.exists():
+        clang = Path("/opt/rocm/llvm/bin/clang")
+    gen = SANDIR / "libattn_gen.so"
+    tmp = gen.with_suffix(".so.tmp")
+    _run([clang, "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-pthread", *C_SAN_FLAGS,
+          str(CSRC / "gen" / "normal_gen.c"), "-o", str(tmp), "-lm"])
+    os.replace(tmp, gen)
+    return out
+
+
 def build_all() -> None:
     build_gen()
     build_hip()
     build_probe()
+    build_sanitized()
 
 
 if __name__ == "__main__":
