@@ -28,7 +28,10 @@
 //     write LDS directly, double buffered; 128-byte rows use the same XOR
 //     swizzle of 16-byte chunks as the attention kernels' K tiles (conflict-
 //     free ds_read_b128 operand reads).  The fragments of the next k step
-//     are read while the current step's MFMAs run.
+//     are read while the current step's MFMAs run, and the last k step's
+//     MFMAs of each tile are issued after the next tile's barrier (their
+//     fragments are already in registers), so they cover the barrier and
+//     the first LDS round trip of the next tile.
 //   * Each XCD takes a compact block of output tiles (grouped tile order),
 //     so the X and W tiles it reads are shared through its own L2.
 //   * Tokens past B T and features past N read as zero (range-checked buffer
@@ -147,50 +150,55 @@ qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16*
     // The fragments of k step s + 1 are read (inline assembly, waits bound
     // to the fragment registers) while the 8 MFMAs of step s run; the
     // compiler's own reads were issued only a few MFMAs ahead.
+    // Fragments of the previous tile's last k step: multiplied after the
+    // barrier, while the first reads of the next tile are in flight (the
+    // accumulation order of every output is unchanged).
+    bf16x8 g[6];
     auto tile = [&](int kt, auto stage) {
         constexpr int B = decltype(stage)::value;
         wait_vmem_all();
         __syncthreads();  // tile kt landed for every wave; the other stage is free
         if (kt + 1 < n_kt) issue(kt + 1, B ^ 1);
         bf16x8 f[2][6];  // [ring slot][X block 0, 1, W block 0..3]
-        auto read = [&](bf16x8 (&g)[6], auto step) {
+        auto read = [&](bf16x8 (&r)[6], auto step) {
             constexpr int S = decltype(step)::value;
-            g[0] = ds_read_b128_asm<B * kXTile>(xa[S]);
-            g[1] = ds_read_b128_asm<B * kXTile + 32 * kRowB>(xa[S]);
-#pragma unroll
-            for (int fb = 0; fb < 4; ++fb) {
-                switch (fb) {
-                    case 0: g[2] = ds_read_b128_asm<B * kWTile>(wa[S]); break;
-                    case 1: g[3] = ds_read_b128_asm<B * kWTile + 32 * kRowB>(wa[S]); break;
-                    case 2: g[4] = ds_read_b128_asm<B * kWTile + 64 * kRowB>(wa[S]); break;
-                    default: g[5] = ds_read_b128_asm<B * kWTile + 96 * kRowB>(wa[S]); break;
-                }
-            }
+            r[0] = ds_read_b128_asm<B * kXTile>(xa[S]);
+            r[1] = ds_read_b128_asm<B * kXTile + 32 * kRowB>(xa[S]);
+            r[2] = ds_read_b128_asm<B * kWTile>(wa[S]);
+            r[3] = ds_read_b128_asm<B * kWTile + 32 * kRowB>(wa[S]);
+            r[4] = ds_read_b128_asm<B * kWTile + 64 * kRowB>(wa[S]);
+            r[5] = ds_read_b128_asm<B * kWTile + 96 * kRowB>(wa[S]);
         };
-        auto mma = [&](bf16x8 (&g)[6]) {
+        auto mma = [&](bf16x8 (&r)[6]) {
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb) {
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
-                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g[2 + fb], g[tb], acc[fb][tb], 0, 0, 0);
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[2 + fb], r[tb], acc[fb][tb], 0, 0, 0);
             }
         };
         read(f[0], std::integral_constant<int, 0>{});
+        if (kt > 0) mma(g);
         read(f[1], std::integral_constant<int, 1>{});
         lds_wait_bind6<6>(f[0]);
         mma(f[0]);
         read(f[0], std::integral_constant<int, 2>{});
         lds_wait_bind6<6>(f[1]);
         mma(f[1]);
-        read(f[1], std::integral_constant<int, 3>{});
+        read(g, std::integral_constant<int, 3>{});
         lds_wait_bind6<6>(f[0]);
         mma(f[0]);
-        lds_wait_bind6<0>(f[1]);
-        mma(f[1]);
+        lds_wait_bind6<0>(g);  // before the next barrier: stage B is refilled after it
     };
     for (int kt = 0; kt < n_kt; kt += 2) {
         tile(kt, std::integral_constant<int, 0>{});
         if (kt + 1 < n_kt) tile(kt + 1, std::integral_constant<int, 1>{});
+    }
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+            acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g[2 + fb], g[tb], acc[fb][tb], 0, 0, 0);
     }
 
     // Epilogue: lane (token column l32, half hi) holds features
