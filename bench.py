@@ -700,24 +700,34 @@ def profile_record(name):
 
 def ceilings(torch, stream, dev, run_prefill=None):
     """Measured ceilings beside the published peaks: a register-fed bf16 MFMA
-    loop (TFLOP/s and its shader clock), a 1 GiB streaming read (GB/s, the
-    decode kernel's load pattern), and the shader clock sampled while the
-    prefill runs."""
+    loop with low-entropy operands and the same with random bf16 operands
+    (TFLOP/s and shader clock of each: the power limit, and so the clock,
+    depends on the operand bits), a 1 GiB streaming read (GB/s, the decode
+    kernel's load pattern), and the shader clock sampled while the prefill
+    runs."""
     from transformer_scaled_dot_flash_amd import probe
     probe.load_library()
-    n_wg, iters = 1024, 4000
+    n_wg = 1024
     out = torch.empty(n_wg * 512, dtype=torch.float32, device=dev)
     cyc = torch.zeros(n_wg * 8 * 2, dtype=torch.int64, device=dev)
-    for _ in range(3):  # warm-up, then the timed launch
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        probe.attn_probe_mfma(n_wg, iters, out, cyc, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    flops = n_wg * 8 * iters * 4 * 32768
-    c = cyc.view(-1, 2).double()
-    mfma_clock = float((c[:, 0] / (c[:, 1] * 10.0)).median())  # reference clock: 100 MHz
+
+    def mfma_rate(fn, iters, mfma_per_iter):
+        # two warm-up launches, then the median of three timed ones
+        runs = []
+        for i in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(n_wg, iters, out, cyc, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                c = cyc.view(-1, 2).double()
+                runs.append((e0.elapsed_time(e1), float((c[:, 0] / (c[:, 1] * 10.0)).median())))  # ref: 100 MHz
+        ms, clock = sorted(runs)[1]
+        return n_wg * 8 * iters * mfma_per_iter * 32768 / (ms * 1e-3) / 1e12, clock
+
+    mfma_tf, mfma_clock = mfma_rate(probe.attn_probe_mfma, 4000, 4)
+    rand_tf, rand_clock = mfma_rate(probe.attn_probe_mfma_random, 500, 32)
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.empty(4096, dtype=torch.int32, device=dev)
@@ -730,7 +740,8 @@ def ceilings(torch, stream, dev, run_prefill=None):
         torch.cuda.synchronize()
         if i >= 2:
             times.append(e0.elapsed_time(e1))
-    res = {"mfma_bf16_tflops": round(flops / (ms * 1e-3) / 1e12, 1), "mfma_clock_ghz": round(mfma_clock, 3),
+    res = {"mfma_bf16_tflops": round(mfma_tf, 1), "mfma_clock_ghz": round(mfma_clock, 3),
+           "mfma_bf16_random_tflops": round(rand_tf, 1), "mfma_random_clock_ghz": round(rand_clock, 3),
            "stream_read_gbs": round(nbytes / (sorted(times)[len(times) // 2] * 1e-3) / 1e9, 1),
            "published_bf16_tflops": PEAK_BF16_TFLOPS, "published_hbm_gbs": PEAK_HBM_GBS,
            "published_clock_ghz": 2.4}
@@ -962,6 +973,11 @@ def main():
     if paged is not None:
         result["paged_decode"] = paged
     result.update(extra)
+    c = extra.get("ceilings")
+    if do_p and c and c.get("mfma_bf16_random_tflops"):
+        # the same achieved rate against the measured random-operand MFMA ceiling (context; `frac`
+        # stays against the published peak)
+        result["roofline"]["frac_of_measured_random_mfma"] = round(p_tflops / c["mfma_bf16_random_tflops"], 4)
     parity = {}
     if do_d and not args.no_parity:
         # the decode workload's output of the timed calls, every element against the oracle

@@ -27,6 +27,13 @@ extern "C" {
  *           reference ticks over its loop */
 int attn_probe_mfma(int n_wg, int iters, float* out, unsigned long long* cycles, void* stream);
 
+/* The same with pseudo-random bf16 operands spread like N(0,1) (eight
+ * register sets, both operands change on every MFMA): every wave runs
+ * iters x 32 MFMAs.  The chip's power limit, and so its clock, depends on
+ * the operand bits, so this is the matrix-core ceiling for random data.
+ * Same arguments and outputs as attn_probe_mfma. */
+int attn_probe_mfma_random(int n_wg, int iters, float* out, unsigned long long* cycles, void* stream);
+
 /* Reads bytes of src once (16-byte non-temporal loads written straight to
  * LDS, the decode kernel's access pattern), split over n_wg workgroups of
  * 4 waves; bytes / n_wg must be a multiple of 64 KiB and below 2 GiB.

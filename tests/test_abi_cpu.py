@@ -325,6 +325,9 @@ def test_probe_rejects_bad_arguments_before_launching():
     inval = 1  # hipErrorInvalidValue
     assert lib.attn_probe_mfma(0, 10, 0x1000, 0x2000, None) == inval
     assert lib.attn_probe_mfma(4, 10, None, 0x2000, None) == inval
+    assert lib.attn_probe_mfma_random(0, 10, 0x1000, 0x2000, None) == inval
+    assert lib.attn_probe_mfma_random(4, 0, 0x1000, 0x2000, None) == inval
+    assert lib.attn_probe_mfma_random(4, 10, 0x1000, None, None) == inval
     assert lib.attn_probe_stream_read(0x1000, 1 << 20, 0x2000, 3, None) == inval   # not a 64 KiB multiple per WG
     assert lib.attn_probe_stream_read(0x1000, 0, 0x2000, 4, None) == inval
     assert lib.attn_probe_stream_read(None, 1 << 26, 0x2000, 4, None) == inval

@@ -8,6 +8,13 @@
 //                          on register operands; 8 waves per workgroup (two
 //                          per SIMD); writes one checksum per lane and the
 //                          shader-clock / 100 MHz-clock cycles of each wave
+//   attn_probe_mfma_random the same rate with operands of the attention
+//                          workloads' kind: eight register sets of pseudo-
+//                          random bf16 values (spread like N(0,1)), so both
+//                          operands change on every MFMA.  The chip's power
+//                          limit depends on the operand bits the matrix cores
+//                          switch, so this rate and its clock are the
+//                          ceiling that random bf16 data can reach
 //   attn_probe_stream_read reads `bytes` (a multiple of 16 MiB) once with
 //                          16-byte loads written straight to LDS (non-
 //                          temporal), as the decode kernel streams its cache;
@@ -43,6 +50,60 @@ __global__ __launch_bounds__(512) void mfma_kernel(float* out, unsigned long lon
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+    }
+    float s = 0.f;
+    for (int k = 0; k < 4; ++k)
+        for (int j = 0; j < 16; ++j) s += acc[k][j];
+    const unsigned long long t1 = __builtin_readcyclecounter();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    out[(size_t)blockIdx.x * 512 + threadIdx.x] = s;
+    if (lane == 0) {
+        cyc[((size_t)blockIdx.x * 8 + wave) * 2] = t1 - t0;
+        cyc[((size_t)blockIdx.x * 8 + wave) * 2 + 1] = r1 - r0;
+    }
+}
+
+// Integer hash (xorshift-multiply) of the lane's operand index.
+__device__ inline uint32_t hash32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352dU;
+    x ^= x >> 15;
+    x *= 0x846ca68bU;
+    x ^= x >> 16;
+    return x;
+}
+// A value in (-2.4, 2.4) with a triangular density (sum of two uniforms):
+// bf16 bit patterns like those of N(0,1) inputs.
+__device__ inline __bf16 spread(uint32_t h) {
+    const float u = (float)(h & 0xffffu) * (1.f / 65536.f) + (float)(h >> 16) * (1.f / 65536.f) - 1.f;
+    return (__bf16)(2.4f * u);
+}
+
+__global__ __launch_bounds__(512) void mfma_random_kernel(float* out, unsigned long long* cyc, int iters) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    f32x16 acc[4] = {};
+    bf16x8 a[8], b[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t h = hash32((uint32_t)(blockIdx.x * 4096u + threadIdx.x * 64u + r * 8u + i));
+            a[r][i] = spread(h);
+            b[r][i] = spread(hash32(h));
+        }
+    }
+    const unsigned long long t0 = __builtin_readcyclecounter();
+    const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+        // 32 MFMAs: chain k takes A set r and B set r + k, so consecutive
+        // MFMAs never repeat an operand
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b[(r + k) & 7], acc[k], 0, 0, 0);
+        }
     }
     float s = 0.f;
     for (int k = 0; k < 4; ++k)
@@ -108,6 +169,13 @@ int attn_probe_mfma(int n_wg, int iters, float* out, unsigned long long* cycles,
     if (n_wg <= 0 || iters <= 0 || !out || !cycles) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(mfma_kernel, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream), out, cycles,
                        iters);
+    return (int)hipGetLastError();
+}
+
+int attn_probe_mfma_random(int n_wg, int iters, float* out, unsigned long long* cycles, void* stream) {
+    if (n_wg <= 0 || iters <= 0 || !out || !cycles) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_random_kernel, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream), out,
+                       cycles, iters);
     return (int)hipGetLastError();
 }
 

@@ -7,7 +7,7 @@ import ctypes
 from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "_lib" / "libattn_probe.so"
-EXPORTED = ("attn_probe_mfma", "attn_probe_stream_read", "attn_probe_clock")
+EXPORTED = ("attn_probe_mfma", "attn_probe_mfma_random", "attn_probe_stream_read", "attn_probe_clock")
 
 _lib = None
 
@@ -26,6 +26,7 @@ def load_library(path: Path | str | None = None):
     lib = ctypes.CDLL(str(p))
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.attn_probe_mfma.argtypes = [i, i, vp, vp, vp]
+    lib.attn_probe_mfma_random.argtypes = [i, i, vp, vp, vp]
     lib.attn_probe_stream_read.argtypes = [vp, sz, vp, i, vp]
     lib.attn_probe_clock.argtypes = [vp, i, vp]
     for f in EXPORTED:
@@ -50,6 +51,11 @@ def _check(rc, where):
 
 def attn_probe_mfma(n_wg, iters, out, cycles, stream=None):
     _check(load_library().attn_probe_mfma(n_wg, iters, _ptr(out), _ptr(cycles), _stream(stream)), "attn_probe_mfma")
+
+
+def attn_probe_mfma_random(n_wg, iters, out, cycles, stream=None):
+    _check(load_library().attn_probe_mfma_random(n_wg, iters, _ptr(out), _ptr(cycles), _stream(stream)),
+           "attn_probe_mfma_random")
 
 
 def attn_probe_stream_read(src, nbytes, sink, n_wg, stream=None):
