@@ -75,6 +75,22 @@ def traffic_from_profile(name, digest):
     return d.get("hbm_bytes_per_launch")
 
 
+def counters_from_profile(name, digest):
+    """Matrix-core busy fraction and shader clock from the committed shader
+    counters of a kernel (profiles/<name>_counters.json), or None when they
+    are missing or were taken on different kernel source."""
+    f = PROFILES / f"{name}_counters.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("source_sha256") != digest:
+        return None
+    busy = d["counters_per_dispatch"].get("SQ_VALU_MFMA_BUSY_CYCLES")
+    cyc = d.get("shader_cycles_per_launch")
+    return {"mfma_busy": round(busy / (cyc * 1024), 3) if busy and cyc else None,
+            "shader_clock_ghz": d.get("shader_clock_ghz"), "source": f"profiles/{name}_counters.md"}
+
+
 def cpu_info():
     """Host facts for the CPU baseline: logical CPUs, CPUs this process may
     run on, the BLAS thread pool numpy uses, and the CPU model."""
@@ -948,6 +964,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profile("prefill_bf16_T8192_D128_gqa", prefill_digest),
+            # matrix cores busy and shader clock under the committed counter runs (which run a few
+            # percent slower than the timed calls): the published peak assumes 100% busy at 2.4 GHz
+            "counters": counters_from_profile("prefill_bf16_T8192_D128_gqa", prefill_digest),
             "avg_launch_us": round(p_avg * 1e3, 2),
             "min_launch_us": round(min(p_ms) * 1e3, 2),
             **percentiles_us(p_ms, "launch"),
