@@ -538,6 +538,8 @@ def time_paged_decode(abi, torch, wd, kd, vd, qd, od_contig, stream, dev, warmup
         pool[perm] = logical
         return pool
     kpool, vpool = scatter(kd), scatter(vd)
+    pools = [(kpool, vpool), (kpool.clone(), vpool.clone())]  # alternated: no reuse through the Infinity Cache
+    n_call = [0]
     table = perm.view(B, per).to(torch.int32).contiguous()
     lens = torch.full((B,), T, dtype=torch.int32, device=dev)
     q2 = qd.view(B, wd.H_q, D)
@@ -546,7 +548,9 @@ def time_paged_decode(abi, torch, wd, kd, vd, qd, od_contig, stream, dev, warmup
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def run():
-        abi.attn_fwd_decode_paged(q2, kpool, vpool, o2, table, lens, B, wd.H_q, H_kv, D, PAGE_SIZE,
+        kp_, vp_ = pools[n_call[0] % 2]
+        n_call[0] += 1
+        abi.attn_fwd_decode_paged(q2, kp_, vp_, o2, table, lens, B, wd.H_q, H_kv, D, PAGE_SIZE,
                                   n_pages, per, wd.scale, abi.ATTN_BF16, 0, ws, ws_bytes, stream)
 
     log("paged decode: warmup")
@@ -577,7 +581,8 @@ def time_paged_decode(abi, torch, wd, kd, vd, qd, od_contig, stream, dev, warmup
         "value": round(gbs, 1),
         "unit": "GB/s",
         "config": {"workload": f"decode B={B} H_q={wd.H_q} H_kv={H_kv} T_kv={T} D={D} bf16, "
-                               f"pages of {PAGE_SIZE} tokens in a shuffled pool of {n_pages}",
+                               f"pages of {PAGE_SIZE} tokens in a shuffled pool of {n_pages} "
+                               "(two identical pools, alternated call by call)",
                    "bytes": nbytes},
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128, paged>",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -670,8 +675,14 @@ def long_decode_line(abi, torch, np, stream, dev, warmup, settle, steps):
     ws_bytes = abi.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T, D, abi.ATTN_BF16, 0)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
+    kv_sets = [(k, v), (k.clone(), v.clone())]  # alternated: no reuse through the Infinity Cache
+    n_call = [0]
+
     def run():
-        abi.attn_fwd_decode(q, k, v, o, B, H_q, H_kv, 1, T, D, False, scale, abi.ATTN_BF16, 0, ws, ws_bytes, stream)
+        k_, v_ = kv_sets[n_call[0] % 2]
+        n_call[0] += 1
+        abi.attn_fwd_decode(q, k_, v_, o, B, H_q, H_kv, 1, T, D, False, scale, abi.ATTN_BF16, 0, ws, ws_bytes,
+                            stream)
     log(f"long decode B={B} T_kv={T} ({splits} splits)")
     avg, mn = time_calls(torch, stream, run, warmup, settle, max(steps, 50))
     kv_bytes = 2 * 2 * B * H_kv * T * D
@@ -679,7 +690,8 @@ def long_decode_line(abi, torch, np, stream, dev, warmup, settle, steps):
     gbs = nbytes / (avg * 1e-3) / 1e9
     part_bytes = 2 * B * H_q * splits * (D + 2) * 4  # partials written by the split pass, read by the combine
     line = {"metric": "long-context decode KV-read GB/s", "value": round(gbs, 1), "unit": "GB/s",
-            "config": {"workload": f"decode B={B} H_q={H_q} H_kv={H_kv} T_kv={T} D={D} bf16", "splits": splits,
+            "config": {"workload": f"decode B={B} H_q={H_q} H_kv={H_kv} T_kv={T} D={D} bf16 (two identical "
+                                   "K/V caches, alternated call by call)", "splits": splits,
                        "bytes": nbytes, "partials_bytes": part_bytes,
                        "partials_share_of_bytes": round(part_bytes / nbytes, 5)},
             "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
@@ -850,8 +862,15 @@ def main():
         abi.attn_fwd_prefill(qp, kp, vp, op, wp.B, wp.H_q, wp.H_kv, wp.T_q, wp.T_kv, wp.D, wp.causal,
                              wp.scale, abi.ATTN_BF16, stream)
 
+    # The decode calls alternate between two identical copies of the 1 GiB K/V cache, so no call
+    # finds its cache in the 256 MB Infinity Cache from the call before.
+    kv_sets = [(kd, vd), (kd.clone(), vd.clone())] if args.only in (None, "decode") else [(kd, vd)]
+    n_dec = [0]
+
     def run_decode():
-        abi.attn_fwd_decode(qd, kd, vd, od, wd.B, wd.H_q, wd.H_kv, 1, wd.T_kv, wd.D, False, wd.scale,
+        k_, v_ = kv_sets[n_dec[0] % len(kv_sets)]
+        n_dec[0] += 1
+        abi.attn_fwd_decode(qd, k_, v_, od, wd.B, wd.H_q, wd.H_kv, 1, wd.T_kv, wd.D, False, wd.scale,
                             abi.ATTN_BF16, 0, ws, ws_bytes, stream)
 
     # Untimed warm-up: W steps, continued until the GPU clock has settled
@@ -948,7 +967,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "prefill: causal GQA B=1 H_q=32 H_kv=8 T=8192 D=128 bf16 (scale 1/sqrt(128)); "
-                        "decode: B=64 H_q=32 H_kv=8 T_q=1 T_kv=4096 D=128 bf16",
+                        "decode: B=64 H_q=32 H_kv=8 T_q=1 T_kv=4096 D=128 bf16 (two identical K/V caches, "
+                        "alternated call by call)",
             "prefill_flops": wp.flops(),
             "decode_bytes": wd.bytes(),
             "decode_splits": n_splits,
