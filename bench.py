@@ -648,7 +648,7 @@ def small_prefill_lines(abi, torch, np, stream, dev, warmup, settle, steps):
                 "tflops": round(tf, 2),
                 "config": {"workload": w.name, "flops": w.flops(), "bytes": w.bytes()},
                 "roofline": {"bound": "alu" if w.dtype == "f32" else "mfma",
-                             "kernel": "attn_f32_kernel<64>" if w.dtype == "f32" else "prefill_bf16_kernel<D=64,causal,BN=64,8 waves in 2 key groups>",
+                             "kernel": "attn_f32_row_kernel<64> (one wave per row)" if w.dtype == "f32" else "prefill_bf16_kernel<D=64,causal,BN=64,8 waves in 2 key groups>",
                              "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                              "frac": round(tf / peak, 5), "traffic": None,
                              "avg_launch_us": round(avg * 1e3, 2), "min_launch_us": round(mn * 1e3, 2)}}

@@ -118,6 +118,9 @@ PREFILL_CASES = [
     (2, 4, 2, 100, 100, 128, True, "f32"),
     (1, 6, 3, 77, 130, 64, True, "f32"),
     (1, 4, 1, 33, 33, 128, False, "f32"),
+    # fp32 above 2^24 (row, key) pairs: the 64-rows-per-workgroup kernel instead of one wave per row
+    (1, 4, 2, 2100, 2100, 64, True, "f32"),
+    (1, 2, 1, 1500, 6000, 128, False, "f32"),
 ]
 
 
