@@ -451,6 +451,35 @@ def time_calls(torch, stream, run, warmup, settle, steps):
     return sum(ms) / steps, min(ms)
 
 
+def graph_call_us(torch, dev, run_on, out, n_calls=20, reps=7):
+    """GPU time per call (us) with ``n_calls`` calls captured into one HIP
+    graph and replayed (no host launch cost between kernels): the median over
+    ``reps`` timed replays, after a warm-up replay.  Also returns whether
+    every replay left ``out`` equal, bit for bit, to an eager call's output."""
+    cur = torch.cuda.current_stream(dev)
+    run_on(cur)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream(device=dev)  # default priority
+    side.wait_stream(cur)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(n_calls):
+            run_on(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    times, same = [], True
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        same = same and bool(torch.equal(out.view(torch.int16), ref.view(torch.int16)))
+        if i:
+            times.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+    return sorted(times)[len(times) // 2], same
+
+
 def mfma_line(metric, workload, flops, avg, mn, kernel):
     tf = flops / (avg * 1e-3) / 1e12
     return {"metric": metric, "value": round(tf, 1), "unit": "TFLOP/s",
@@ -637,11 +666,15 @@ def small_prefill_lines(abi, torch, np, stream, dev, warmup, settle, steps):
         od = torch.empty_like(qd)
         code = abi.ATTN_BF16 if w.dtype == "bf16" else abi.ATTN_F32
 
-        def run():
+        def run_on(st, qd=qd, kd=kd, vd=vd, od=od, w=w, code=code):
             abi.attn_fwd_prefill(qd, kd, vd, od, w.B, w.H_q, w.H_kv, w.T_q, w.T_kv, w.D, w.causal, w.scale,
-                                 code, stream)
+                                 code, st)
+
+        def run():
+            run_on(stream)
         log(f"small prefill {w.name}")
         avg, mn = time_calls(torch, stream, run, max(warmup, 20), settle, max(steps, 50))
+        g_us, g_same = graph_call_us(torch, dev, run_on, od)
         tf = w.flops() / (avg * 1e-3) / 1e12
         peak = PEAK_F32_VALU_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
         line = {"metric": "prefill call latency (us) and TFLOP/s", "value": round(avg * 1e3, 2), "unit": "us",
@@ -651,7 +684,10 @@ def small_prefill_lines(abi, torch, np, stream, dev, warmup, settle, steps):
                              "kernel": "attn_f32_row_kernel<64> (one wave per row)" if w.dtype == "f32" else "prefill_bf16_kernel<D=64,causal,BN=64,8 waves in 2 key groups>",
                              "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                              "frac": round(tf / peak, 5), "traffic": None,
-                             "avg_launch_us": round(avg * 1e3, 2), "min_launch_us": round(mn * 1e3, 2)}}
+                             "avg_launch_us": round(avg * 1e3, 2), "min_launch_us": round(mn * 1e3, 2)},
+                # 20 calls captured into one HIP graph and replayed: GPU time per call without the
+                # host's launch cost between them; the replays' output equals an eager call's
+                "graph_us_per_call": round(g_us, 2), "graph_output_equals_eager": g_same}
         if ordinal == 3:
             line["roofline"]["traffic"] = profile_traffic("prefill_bf16_gpt2s_B4_H12_T1024_D64")
         out[w.name] = line
