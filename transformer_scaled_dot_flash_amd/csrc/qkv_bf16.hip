@@ -31,7 +31,8 @@
 //     are read while the current step's MFMAs run, and the last k step's
 //     MFMAs of each tile are issued after the next tile's barrier (their
 //     fragments are already in registers), so they cover the barrier and
-//     the first LDS round trip of the next tile.
+//     the first LDS round trip of the next tile; the 8 loads of the tile
+//     after that go out between those MFMAs, one after each.
 //   * Each XCD takes a compact block of output tiles (grouped tile order),
 //     so the X and W tiles it reads are shared through its own L2.
 //   * Tokens past B T and features past N read as zero (range-checked buffer
@@ -108,6 +109,18 @@ qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16*
     // 1 KiB, 4 + 4 per wave.  LDS holds the X tiles of both stages, then
     // the W tiles of both stages, so every operand read's stage and block
     // offset fits the 16-bit immediate of ds_read_b128.
+    // Load i (0 .. 2 NL - 1) of k tile kt alone: i < NL a piece of X, else of W.
+    auto issue_one = [&](int kt, int buf, int i) {
+        constexpr int NL = kXTile / (1024 * kWaves);
+        const int n = i % NL;
+        const int blk = wave * NL + n;
+        const int p = blk * 64 + lane;
+        const int row = p / kCPR;
+        const int logical = (p % kCPR) ^ swz<kCPR>(row);
+        const uint32_t off = (uint32_t)row * rowb + (uint32_t)kt * kRowB + logical * 16;
+        if (i < NL) buf_load_lds16(rX, smem + buf * kXTile + blk * 1024, off);
+        else buf_load_lds16(rW, smem + 2 * kXTile + buf * kWTile + blk * 1024, off);
+    };
     auto issue = [&](int kt, int buf) {
         unsigned char* xs = smem + buf * kXTile;
         unsigned char* ws = smem + 2 * kXTile + buf * kWTile;
@@ -158,7 +171,6 @@ qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16*
         constexpr int B = decltype(stage)::value;
         wait_vmem_all();
         __syncthreads();  // tile kt landed for every wave; the other stage is free
-        if (kt + 1 < n_kt) issue(kt + 1, B ^ 1);
         bf16x8 f[2][6];  // [ring slot][X block 0, 1, W block 0..3]
         auto read = [&](bf16x8 (&r)[6], auto step) {
             constexpr int S = decltype(step)::value;
@@ -178,7 +190,27 @@ qkv_project_kernel(const bf16* __restrict__ X, const bf16* __restrict__ W, bf16*
             }
         };
         read(f[0], std::integral_constant<int, 0>{});
-        if (kt > 0) mma(g);
+        // The previous tile's last step with tile kt + 1's loads between its
+        // MFMAs, one after each (+2.9% over issuing the 8 loads together
+        // right after the barrier).
+        const bool more = kt + 1 < n_kt;
+        if (kt > 0) {
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g[2 + fb], g[tb], acc[fb][tb], 0, 0, 0);
+                    if (more) issue_one(kt + 1, B ^ 1, fb * 2 + tb);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one vector-memory read
+            }
+        } else if (more) {
+            issue(kt + 1, B ^ 1);
+        }
         read(f[1], std::integral_constant<int, 1>{});
         lds_wait_bind6<6>(f[0]);
         mma(f[0]);
