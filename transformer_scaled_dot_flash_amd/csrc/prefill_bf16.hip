@@ -237,8 +237,6 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const uint32_t q_bytes = (uint32_t)((T_q - 1) * SQ + D) * 2;
     const uint32_t kv_bytes = T_kv > 0 ? (uint32_t)((T_kv - 1) * SK + D) * 2 : 0u;
     const auto rQ = make_rsrc(Q + q_base, q_bytes);
-    const auto rK = make_rsrc(K + kv_base, kv_bytes);
-    const auto rV = make_rsrc(V + kv_base, kv_bytes);
     const auto rO = make_rsrc(O + q_base, q_bytes);
 
     const int off = T_kv - T_q;  // bottom-right causal alignment
@@ -286,19 +284,27 @@ prefill_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
     // Direct-to-LDS loads of one K or V tile.  Keys past T_kv are outside
     // the buffer range and load as zero.  Tile t uses ring slot (t - t_lo) & 1.
-    auto issue = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int t) {
-        const int j0 = t * BN;
+    // The tile's first row is folded into a per-tile buffer resource (base
+    // moved to it, range shortened by as much, scalar arithmetic), so each
+    // lane's offset within the tile is a constant and the loads need no
+    // vector address arithmetic; the range check still zeroes keys past T_kv.
+    uint32_t loff[NLD];
 #pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const int blk = wave * NLD + n;
-            const int p = blk * 64 + lane;  // chunk slot in the tile
-            const int row = p / CPR;
-            const int logical = (p % CPR) ^ swz<CPR>(row);
-            buf_load_lds16(r, dst + blk * 1024, (uint32_t)(j0 + row) * SK * 2 + logical * 16);
-        }
+    for (int n = 0; n < NLD; ++n) {
+        const int blk = wave * NLD + n;
+        const int p = blk * 64 + lane;  // chunk slot in the tile
+        const int row = p / CPR;
+        const int logical = (p % CPR) ^ swz<CPR>(row);
+        loff[n] = (uint32_t)row * SK * 2 + logical * 16;
+    }
+    auto issue = [&](const bf16* base, unsigned char* dst, int t) {
+        const uint32_t off = (uint32_t)__builtin_amdgcn_readfirstlane(t * BN) * (uint32_t)(SK * 2);
+        const auto r = make_rsrc(reinterpret_cast<const unsigned char*>(base) + off, kv_bytes - off);
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) buf_load_lds16(r, dst + (wave * NLD + n) * 1024, loff[n]);
     };
-    auto issue_k = [&](int t) { issue(rK, kring + ((t - t_lo) & 1) * TILE, t); };
-    auto issue_v = [&](int t) { issue(rV, vring + ((t - t_lo) & 1) * TILE, t); };
+    auto issue_k = [&](int t) { issue(K + kv_base, kring + ((t - t_lo) & 1) * TILE, t); };
+    auto issue_v = [&](int t) { issue(V + kv_base, vring + ((t - t_lo) & 1) * TILE, t); };
 
     // Prologue: K(t_lo), V(t_lo).  Step t issues K(t+1), V(t+1) into the
     // slots of tile t-1, read for the last time in step t-1.  (Each key group
