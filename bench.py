@@ -425,7 +425,7 @@ def profile_traffic(name):
     _, files = KERNELS[name]
     csrc = ROOT / "transformer_scaled_dot_flash_amd" / "csrc"
     return traffic_from_profile(name, source_digest([csrc / f for f in files]))
-LONG_DECODE = (4, 32, 8, 32768, 128, 16)  # B, H_q, H_kv, T_kv, D, default split count
+LONG_DECODE = (4, 32, 8, 32768, 128, 24)  # B, H_q, H_kv, T_kv, D, default split count
 WINDOW = 4096                 # sliding-window line: Mistral-style 4K window
 VARLEN_TOKENS = 32768         # packed-batch line: total query tokens
 
@@ -696,7 +696,7 @@ def small_prefill_lines(abi, torch, np, stream, dev, warmup, settle, steps):
 
 def long_decode_line(abi, torch, np, stream, dev, warmup, settle, steps):
     """Long-context decode whose default plan splits the keys: B=4 H_q=32
-    H_kv=8 T_kv=32768 D=128 bf16 (32 (batch, kv head) groups, 16 splits):
+    H_kv=8 T_kv=32768 D=128 bf16 (32 (batch, kv head) groups, 24 splits):
     the split pass writes per-split partials, the combine pass merges them."""
     from transformer_scaled_dot_flash_amd import inputs
     B, H_q, H_kv, T, D, S_expect = LONG_DECODE

@@ -200,7 +200,7 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
  * runs on until the process ends; the first call on a device looks up that
  * device's copy (hipGetSymbolAddress, with the stream's device current).  A
  * split plan needing more (B * H_q * splits * (D + 2) * 4 bytes; the default
- * plan needs at most about 8.5 MiB) returns ATTN_ERR_SCRATCH before anything
+ * plan needs at most about 12.2 MiB) returns ATTN_ERR_SCRATCH before anything
  * is launched.  All calls on one GPU share its array, and nothing in it has
  * to start at zero: calls that may run at the same time on one GPU (other
  * streams, other threads) race on it and must be ordered by the caller.

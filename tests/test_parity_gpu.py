@@ -401,12 +401,12 @@ def test_library_loaded_before_torch_in_a_fresh_process():
 
 def test_decode_split_merge_with_reused_workspace():
     """One workspace, first filled with 0xFF bytes, serves five split decodes
-    (16 splits) on different inputs: every output matches the oracle and a
+    (the default plan: 19 splits) on different inputs: every output matches the oracle and a
     fresh-workspace call bit for bit (nothing is carried over between
     calls)."""
     import torch
     B, H_q, H_kv, T, D = 4, 32, 8, 3000, 128
-    assert abi.attn_fwd_decode_default_splits(B, H_q, H_kv, T, D) == 16
+    assert abi.attn_fwd_decode_default_splits(B, H_q, H_kv, T, D) == 19
     nbytes = abi.attn_fwd_decode_workspace_bytes(B, H_q, H_kv, T, D, abi.ATTN_BF16, 0)
     ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
     scale = float(np.float32(1.0 / math.sqrt(D)))

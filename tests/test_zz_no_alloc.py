@@ -47,7 +47,7 @@ def test_noalloc_matches_workspace_decode_twice():
     torch = G.torch_mod()
     stream = torch.cuda.current_stream()
     g = torch.Generator(device="cuda").manual_seed(4242)
-    # 1: long-context decode whose default plan splits the keys (16 splits)
+    # 1: long-context decode whose default plan splits the keys (24 splits)
     B, H_q, H_kv, T_kv, D = 4, 32, 8, 32768, 128
     assert abi.attn_fwd_decode_default_splits(B, H_q, H_kv, T_kv, D) > 1
     q = torch.randn(B, H_q, 1, D, device="cuda", generator=g).to(torch.bfloat16)

@@ -15,7 +15,6 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int kMaxSplits = 1024;
 constexpr int kDecodeBlock = 32;  // keys per decode tile; splits are multiples of it
-constexpr int kDecodeWaves = 512; // target decode waves (2 per CU)
 
 size_t elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
@@ -79,14 +78,19 @@ struct SplitPlan {
     int keys_per_split;
 };
 
-int default_splits(int B, int H_q, int H_kv, int T_kv) {
+int default_splits(int B, int H_q, int H_kv, int T_kv, int D) {
     const int G = H_q / H_kv;
     const long long groups = (long long)B * H_kv * ((G + 31) / 32);
     const int n_blocks = (T_kv + kDecodeBlock - 1) / kDecodeBlock;
-    // One wave per (group, split); about 512 waves (two per CU) stream the
-    // cache at full HBM rate.  Enough groups -> one split and no combine
-    // pass; fewer -> split the keys, keeping >= 4 tiles per split.
-    long long want = (kDecodeWaves + groups - 1) / groups;
+    // One wave per (group, split).  The cache streams fastest with one full
+    // round of waves: 768 at D = 128 (three per CU), 1024 at D = 64 (four);
+    // measured over split counts 1..128 on eleven shapes, 512 waves ran 3-6%
+    // (D = 128) and up to a third (D = 64) slower, and a partial second round
+    // (e.g. 1024 waves at D = 128) 15-20% slower.  So: as many splits as fit
+    // in one round (at least one; enough groups -> one split and no combine
+    // pass), keeping >= 4 tiles per split.
+    const long long target = D == 64 ? 1024 : 768;
+    long long want = target / groups;
     long long cap = n_blocks / 4;
     if (cap < 1) cap = 1;
     if (want > cap) want = cap;
@@ -95,9 +99,9 @@ int default_splits(int B, int H_q, int H_kv, int T_kv) {
     return (int)want;
 }
 
-SplitPlan plan_splits(int B, int H_q, int H_kv, int T_kv, int requested) {
+SplitPlan plan_splits(int B, int H_q, int H_kv, int T_kv, int D, int requested) {
     const int n_blocks = (T_kv + kDecodeBlock - 1) / kDecodeBlock;
-    int n = requested > 0 ? requested : default_splits(B, H_q, H_kv, T_kv);
+    int n = requested > 0 ? requested : default_splits(B, H_q, H_kv, T_kv, D);
     if (n > n_blocks) n = n_blocks;
     const int blocks_per = (n_blocks + n - 1) / n;
     SplitPlan p;
@@ -379,7 +383,7 @@ attn_status_t attn_fwd_decode(const void* q, const void* k, const void* v, void*
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == ATTN_F32) return decode_f32(q, k, v, o, B, H_q, H_kv, T_kv, D, scale, s);
 
-    const SplitPlan p = plan_splits(B, H_q, H_kv, T_kv, num_splits);
+    const SplitPlan p = plan_splits(B, H_q, H_kv, T_kv, D, num_splits);
     const size_t need = decode_ws_bytes(B, H_q, D, p);
     if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
     if (need > 0 && misaligned(workspace)) return ATTN_ERR_ALIGNMENT;
@@ -404,7 +408,7 @@ attn_status_t attn_fwd_decode_noalloc(const void* q, const void* k, const void* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == ATTN_F32) return decode_f32(q, k, v, o, B, H_q, H_kv, T_kv, D, scale, s);
 
-    const SplitPlan p = plan_splits(B, H_q, H_kv, T_kv, num_splits);
+    const SplitPlan p = plan_splits(B, H_q, H_kv, T_kv, D, num_splits);
     const size_t need = decode_ws_bytes(B, H_q, D, p);
     if (need > (size_t)ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
     void* ws = nullptr;
@@ -422,12 +426,12 @@ size_t attn_fwd_decode_workspace_bytes(int B, int H_q, int H_kv, int T_kv, int D
     if (check_params(B, H_q, H_kv, 1, T_kv, D, dtype, 1.0f) != ATTN_OK) return 0;
     if (num_splits < 0 || num_splits > kMaxSplits) return 0;
     if (dtype == ATTN_F32) return 0;
-    return decode_ws_bytes(B, H_q, D, plan_splits(B, H_q, H_kv, T_kv, num_splits));
+    return decode_ws_bytes(B, H_q, D, plan_splits(B, H_q, H_kv, T_kv, D, num_splits));
 }
 
 int attn_fwd_decode_default_splits(int B, int H_q, int H_kv, int T_kv, int D) {
     if (check_params(B, H_q, H_kv, 1, T_kv, D, ATTN_BF16, 1.0f) != ATTN_OK) return 0;
-    return plan_splits(B, H_q, H_kv, T_kv, 0).n_splits;
+    return plan_splits(B, H_q, H_kv, T_kv, D, 0).n_splits;
 }
 
 attn_status_t attn_fwd_decode_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -444,7 +448,7 @@ attn_status_t attn_fwd_decode_paged(const void* q, const void* k_pages, const vo
         (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
         return ATTN_ERR_ALIGNMENT;
     const int T_max = max_pages * page_size;
-    const SplitPlan p = plan_splits(B, H_q, H_kv, T_max, num_splits);
+    const SplitPlan p = plan_splits(B, H_q, H_kv, T_max, D, num_splits);
     const size_t need = decode_ws_bytes(B, H_q, D, p);
     if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
     if (need > 0 && misaligned(workspace)) return ATTN_ERR_ALIGNMENT;
@@ -485,7 +489,7 @@ size_t attn_fwd_decode_paged_workspace_bytes(int B, int H_q, int H_kv, int D, in
     if (check_paged_params(B, H_q, H_kv, D, page_size, 1, max_pages, ATTN_BF16, 1.0f, num_splits) !=
         ATTN_OK)
         return 0;
-    return decode_ws_bytes(B, H_q, D, plan_splits(B, H_q, H_kv, max_pages * page_size, num_splits));
+    return decode_ws_bytes(B, H_q, D, plan_splits(B, H_q, H_kv, max_pages * page_size, D, num_splits));
 }
 
 attn_status_t attn_qkv_project(const void* x, const void* w, void* q, void* k, void* v, int B,
