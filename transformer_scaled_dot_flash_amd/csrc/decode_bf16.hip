@@ -301,82 +301,104 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     }
 }
 
-// One wave per (batch, q head): merge the split states and write O.  Lane
-// (split group sg = lane / 16, feature group fq = lane % 16) merges splits
-// sg, sg + 4, sg + 8, ... for features fq * D/16 ... with the online form of
-// the merge rule (running base, sum and output), four splits' loads in
-// flight at a time; the four split groups are then merged across lanes
-// (two exchanges) and the first group writes O.
+// Four waves per (batch, q head): merge the split states and write O.  Lane
+// (split group g = 4 * wave + lane / 16, feature group fq = lane % 16)
+// merges splits g, g + 16, g + 32, ... for features fq * D/16 ... with the
+// online form of the merge rule (running base, sum and output), four
+// splits' loads in flight at a time; the four split groups of a wave are
+// merged across lanes (two exchanges), the four waves' states through LDS,
+// and wave 0 writes O.  (One wave per row took twice as long with 125
+// splits: its lanes walked the splits in twice as many dependent rounds.)
+constexpr int kCombineWaves = 4;  // waves per output row in the combine pass
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws_o,
-                                                            const float* __restrict__ ws_ml,
-                                                            bf16* __restrict__ O, int n_splits) {
+__global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(const float* __restrict__ ws_o,
+                                                                           const float* __restrict__ ws_ml,
+                                                                           bf16* __restrict__ O, int n_splits) {
     constexpr int FPL = D / 16;  // features per lane
+    constexpr int NG = 4 * kCombineWaves;  // split groups of the row
+    __shared__ float xs[kCombineWaves][16][FPL + 2];
     const size_t row = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int sg = lane >> 4, fq = lane & 15;
+    const int gsg = wave * 4 + sg;  // this lane's split group
     const float* ml = ws_ml + row * n_splits * 2;
     const float* op = ws_o + row * n_splits * D + fq * FPL;
     float m = -INFINITY, L = 0.f, acc[FPL];
 #pragma unroll
     for (int f = 0; f < FPL; ++f) acc[f] = 0.f;
-    // merge one split state (ms, ls, o) into (m, L, acc)
-    auto merge = [&](float ms, float ls, const f32x4 (&o)[FPL / 4]) {
-        if (ms == -INFINITY) return;  // an empty split (paged sequence shorter than the split start)
+    // merge a state (ms, ls, o) into (m, L, acc); a state with base -inf (an
+    // empty split, or a group with no split) carries nothing
+    auto merge = [&](float ms, float ls, const float (&o)[FPL]) {
+        if (ms == -INFINITY) return;
         const float mn = fmaxf(m, ms);
         const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
         const float w = __builtin_amdgcn_exp2f(ms - mn);
         L = L * a + ls * w;
 #pragma unroll
-        for (int f = 0; f < FPL; ++f) acc[f] = acc[f] * a + o[f / 4][f % 4] * w;
+        for (int f = 0; f < FPL; ++f) acc[f] = acc[f] * a + o[f] * w;
         m = mn;
     };
     constexpr int U = 4;  // splits per lane in flight
-    for (int s0 = sg; s0 < n_splits; s0 += 4 * U) {
+    for (int s0 = gsg; s0 < n_splits; s0 += NG * U) {
         float ms[U], ls[U];
-        f32x4 o[U][FPL / 4];
+        float o[U][FPL];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int sp = s0 + 4 * u;
+            const int sp = s0 + NG * u;
             ms[u] = -INFINITY;
             ls[u] = 0.f;
             if (sp < n_splits) {
                 ms[u] = ml[2 * sp];
                 ls[u] = ml[2 * sp + 1];
 #pragma unroll
-                for (int c = 0; c < FPL / 4; ++c) o[u][c] = *reinterpret_cast<const f32x4*>(op + (size_t)sp * D + 4 * c);
+                for (int c = 0; c < FPL / 4; ++c) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(op + (size_t)sp * D + 4 * c);
+                    o[u][4 * c] = v[0];
+                    o[u][4 * c + 1] = v[1];
+                    o[u][4 * c + 2] = v[2];
+                    o[u][4 * c + 3] = v[3];
+                }
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) merge(ms[u], ls[u], o[u]);
     }
-    // merge the four split groups: lanes lane ^ 16, then lane ^ 32
+    // merge the four split groups of the wave: lanes lane ^ 16, then lane ^ 32
 #pragma unroll
     for (int x = 16; x <= 32; x <<= 1) {
         const float m2 = __shfl_xor(m, x), L2 = __shfl_xor(L, x);
-        f32x4 o2[FPL / 4];
+        float o2[FPL];
 #pragma unroll
-        for (int f = 0; f < FPL; ++f) o2[f / 4][f % 4] = __shfl_xor(acc[f], x);
-        // rescale so (m2, L2, o2) is a merged state, then merge it
-        const float mn = fmaxf(m, m2);
-        const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-        const float b = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
-        L = L * a + L2 * b;
-#pragma unroll
-        for (int f = 0; f < FPL; ++f) acc[f] = acc[f] * a + o2[f / 4][f % 4] * b;
-        m = mn;
+        for (int f = 0; f < FPL; ++f) o2[f] = __shfl_xor(acc[f], x);
+        merge(m2, L2, o2);
     }
-    if (sg == 0) {
-        // every split empty (a paged sequence of length 0): L = 0, O = 0
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        bf16* orow = O + row * D + fq * FPL;
+    // then the waves' states, through LDS, into wave 0
+    if (sg == 0 && wave > 0) {
 #pragma unroll
-        for (int g4 = 0; g4 < FPL / 4; ++g4) {
-            bf16x4 w;
+        for (int f = 0; f < FPL; ++f) xs[wave][fq][f] = acc[f];
+        xs[wave][fq][FPL] = m;
+        xs[wave][fq][FPL + 1] = L;
+    }
+    __syncthreads();
+    if (wave != 0 || sg != 0) return;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) w[q] = (bf16)(acc[4 * g4 + q] * inv);
-            *reinterpret_cast<bf16x4*>(orow + 4 * g4) = w;
-        }
+    for (int w = 1; w < kCombineWaves; ++w) {
+        float o2[FPL];
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) o2[f] = xs[w][fq][f];
+        merge(xs[w][fq][FPL], xs[w][fq][FPL + 1], o2);
+    }
+    // every split empty (a paged sequence of length 0): L = 0, O = 0
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    bf16* orow = O + row * D + fq * FPL;
+#pragma unroll
+    for (int g4 = 0; g4 < FPL / 4; ++g4) {
+        bf16x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (bf16)(acc[4 * g4 + q] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 4 * g4) = w;
     }
 }
 
@@ -392,7 +414,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
                                  a.neg_q, a.paged);
     if (e != hipSuccess || a.n_splits == 1) return e;
     const long long rows = (long long)a.B * a.H_q;
-    return launch_kernel(decode_combine_kernel<D>, dim3((unsigned)rows), dim3(64), 0, s,
+    return launch_kernel(decode_combine_kernel<D>, dim3((unsigned)rows), dim3(64 * kCombineWaves), 0, s,
                          static_cast<const float*>(a.ws_o), static_cast<const float*>(a.ws_ml),
                          static_cast<bf16*>(a.o), a.n_splits);
 }
