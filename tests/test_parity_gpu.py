@@ -150,6 +150,8 @@ DECODE_CASES = [
     (3, 64, 1, 4097, 128, "bf16", 0),   # 64 q heads per kv head: two head blocks
     (1, 40, 5, 777, 64, "bf16", 5),
     (2, 16, 16, 300, 128, "bf16", 0),   # MHA decode
+    (1, 8, 2, 6000, 64, "bf16", 150),   # more than 64 splits: several rounds per combine lane
+    (1, 16, 4, 20000, 64, "bf16", 0),   # default plan at D = 64 with few groups: 125 splits
     (2, 8, 2, 300, 128, "f32", 0),
     (1, 4, 1, 65, 64, "f32", 0),
 ]
