@@ -78,6 +78,7 @@ WINDOW_CASES = [
     (1, 4, 4, 129, 129, 64, 1),       # each row sees only itself
     (1, 4, 1, 700, 700, 128, 255),
     (1, 8, 8, 2048, 2048, 128, 1000),
+    (2, 32, 8, 1100, 1100, 64, 300),  # grid too large for the key split: 4-wave shape
 ]
 
 
