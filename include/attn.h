@@ -284,7 +284,11 @@ size_t attn_fwd_decode_workspace_bytes(int B, int H_q, int H_kv, int T_kv, int D
                                        int dtype, int num_splits);
 
 /* Split count attn_fwd_decode uses when num_splits == 0 (>= 1; 0 for
- * invalid sizes). */
+ * invalid sizes): with G = H_q / H_kv, the B * H_kv * ceil(G / 32) groups
+ * each get as many splits as fit one round of 768 waves (D = 128) or 1024
+ * (D = 64) on the GPU, at least one and at most one per 4 key blocks of
+ * 32; after rounding to whole blocks per split the count may come out
+ * lower. */
 int attn_fwd_decode_default_splits(int B, int H_q, int H_kv, int T_kv, int D);
 
 /* Static, NUL-terminated description of a status code. */
