@@ -134,6 +134,27 @@ def test_decode_workspace_size():
     assert A.attn_fwd_decode_workspace_bytes(1, 64, 1, 4096, 128, BF16, 8) == ws_expected(1, 64, 1, 8, 128)
 
 
+def default_plan(B, H_q, H_kv, T_kv, D):
+    """The default split rule written out: one round of waves (768 at D =
+    128, 1024 at D = 64) over the (batch, kv head, 32-head block) groups, at
+    least one split and at most one per 4 blocks of 32 keys, then whole
+    blocks per split with no empty split."""
+    groups = B * H_kv * -(-(H_q // H_kv) // 32)
+    blocks = -(-T_kv // 32)
+    n = (1024 if D == 64 else 768) // groups
+    n = max(1, min(n, max(1, blocks // 4), 1024))
+    per = -(-blocks // n)
+    return -(-T_kv // (per * 32))
+
+
+@pytest.mark.parametrize("shape", [(4, 32, 8, 32768, 128), (64, 32, 8, 4096, 128), (64, 32, 8, 4096, 64),
+                                   (2, 16, 4, 20000, 64), (16, 32, 8, 8192, 128), (1, 32, 8, 131072, 128),
+                                   (32, 32, 8, 4096, 128), (3, 64, 1, 4097, 128), (4, 32, 8, 3000, 128),
+                                   (1, 1, 1, 1, 64), (1, 8, 1, 200, 128), (1000, 8, 8, 9000, 64)])
+def test_decode_default_split_rule(shape):
+    assert A.attn_fwd_decode_default_splits(*shape) == default_plan(*shape)
+
+
 def test_decode_workspace_too_small_by_one_byte():
     need = A.attn_fwd_decode_workspace_bytes(2, 8, 2, 300, 128, BF16, 0)
     assert decode(ws_bytes=need - 1) == WS
