@@ -25,7 +25,8 @@
 //     LDS directly (no register staging).  Each 1 KiB load covers whole rows;
 //     an XOR swizzle of the 16-byte chunks (chosen through the per-lane
 //     source address) keeps the K reads and the transposing V reads free of
-//     bank conflicts on the 64-bank LDS.
+//     bank conflicts on the 64-bank LDS.  The tile's first row goes into a
+//     per-tile buffer resource, so the lane offsets are constants.
 //   * Each step handles one key tile: scores, weights, O += P V.  The two
 //     waves on each SIMD overlap one another's matrix-core and vector work;
 //     computing the next tile's scores inside the current step (a software
@@ -57,10 +58,13 @@
 //     units are dealt to the XCDs in turn so unequal sequences of a packed
 //     batch spread evenly.
 //
-// Configurations (RB = 1, two waves per SIMD): 8 waves x 32 rows per
-// workgroup and 128-key tiles for long sequences (one K/V tile in LDS serves
-// 256 query rows, one workgroup per CU), 4 waves x 32 rows and 64-key tiles
-// otherwise (two workgroups per CU).  RB = 2 halves the LDS read traffic per
+// Configurations (RB = 1, two waves per SIMD at D = 128): 8 waves x 32 rows
+// per workgroup and 128-key tiles for long sequences (one K/V tile in LDS
+// serves 256 query rows, one workgroup per CU); 8 waves in two key groups of
+// 4 over 128 rows with 64-key tiles for problems whose 128-row workgroups all
+// fit on the GPU at once (the key split halves the longest chain of steps);
+// 4 waves x 32 rows and 64-key tiles otherwise (two workgroups per CU).
+// RB = 2 halves the LDS read traffic per
 // FLOP but needs more than 256 registers per lane, i.e. one wave per SIMD,
 // and was measured slower: a single wave cannot overlap its own softmax with
 // its MFMAs the way two waves of a SIMD overlap each other's.
