@@ -121,6 +121,8 @@ PREFILL_CASES = [
     # fp32 above 2^24 (row, key) pairs: the 64-rows-per-workgroup kernel instead of one wave per row
     (1, 4, 2, 2100, 2100, 64, True, "f32"),
     (1, 2, 1, 1500, 6000, 128, False, "f32"),
+    (1, 1, 1, 4096, 4096, 64, True, "f32"),       # exactly 2^24 pairs: the last size on one wave per row
+    (1, 1, 1, 4096, 4097, 64, True, "f32"),       # one key more: the 64-row kernel
 ]
 
 
