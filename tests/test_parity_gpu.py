@@ -156,6 +156,7 @@ DECODE_CASES = [
     (1, 16, 4, 20000, 64, "bf16", 0),   # default plan at D = 64 with few groups: 125 splits
     (2, 8, 2, 300, 128, "f32", 0),
     (1, 4, 1, 65, 64, "f32", 0),
+    (2, 64, 1, 140000, 64, "f32", 0),   # above 2^24 (row, key) pairs: the 64-row fp32 kernel
 ]
 
 
