@@ -8,6 +8,8 @@
 * ``_lib/san/``            the C ABI and the generator again, with the host code
                            built under AddressSanitizer and UndefinedBehavior-
                            Sanitizer (CPU tests of the host-side validation).
+* ``_lib/c_abi_client``    a plain C client of the C ABI (tests/native), run
+                           by a GPU test.
 
 All are rebuilt when :func:`build_all` is called.  Loading code never
 builds: it raises if a library is missing.
@@ -165,11 +167,27 @@ def build_sanitized(jobs: int = 5) -> Path:
     return out
 
 
+def build_c_client() -> Path:
+    """``_lib/c_abi_client``: a plain C program that calls the C ABI with
+    device memory from the HIP runtime (no torch, no Python); a GPU test runs
+    it.  Host code only, built with gcc against ``libattn.so`` beside it."""
+    out = LIBDIR / "c_abi_client"
+    tmp = out.with_name(out.name + ".tmp")
+    rocm = Path(_hipcc()).resolve().parent.parent
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-I", str(INCLUDE), "-I", str(rocm / "include"),
+          "-D__HIP_PLATFORM_AMD__", str(ROOT / "tests" / "native" / "c_abi_client.c"), "-L", str(LIBDIR), "-lattn",
+          "-L", str(rocm / "lib"), "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{rocm / 'lib'}",
+          "-o", str(tmp)])
+    os.replace(tmp, out)
+    return out
+
+
 def build_all() -> None:
     build_gen()
     build_hip()
     build_probe()
     build_sanitized()
+    build_c_client()
 
 
 if __name__ == "__main__":
