@@ -36,3 +36,14 @@ def test_traffic_records_are_consistent():
         assert abs(rec["hbm_bytes_per_launch"] - total) <= 1  # each figure rounded on its own
         assert rec["algorithmic_bytes_per_launch"] == bench.algorithmic_bytes(name)
         assert rec["avg_duration_us"] >= rec["min_duration_us"] > 0
+
+
+@pytest.mark.parametrize("path", sorted(bench.PROFILES.glob("*_counters.json")), ids=lambda p: p.stem)
+def test_counter_profiles_match_current_kernel_source(path):
+    name = path.stem[: -len("_counters")]
+    sub, files = bench.KERNELS[name]
+    rec = json.loads(path.read_text())
+    assert sub in rec["kernel"]
+    assert rec["source_sha256"] == bench.source_digest([CSRC / f for f in files]), \
+        f"{name}: shader counters taken on other kernel source; re-take them"
+    assert (bench.PROFILES / f"{name}_counters.md").exists()
